@@ -1,0 +1,622 @@
+/*
+ * oracle.c -- plain, slow CPU reference for MXAttention's MXFP4 attention
+ * forward.  TEST INFRASTRUCTURE ONLY (see oracle.h for who may call it).
+ *
+ * Every function follows the pages step by step; the citations name the page
+ * ([P1] the MXAttention paper, [P2] the explainer page, [P3] the MatX
+ * leaky-quantization page) and the section, equation or algorithm.
+ *
+ * Readings of points the pages leave open (each is also listed in the design
+ * notes of the repository):
+ *   - Rotation: Sylvester Hadamard H_d/sqrt(d) in natural order, no random
+ *     signs, evaluated in binary32 with butterfly strides 1,2,..,d/2 and one
+ *     final multiply by fl32(1/sqrt(d)).
+ *   - Element rounding: nearest grid point, exact ties to the even code;
+ *     a value that rounds to zero keeps its sign bit (code 8).
+ *   - E8M0 exponent clamped to [-127, 127]; byte 255 is never produced.
+ *   - Blocks: Q/K along the head dimension; V and P along tokens/keys, in
+ *     32-element blocks aligned to token/key 0, tails padded with +0.
+ *   - The softmax tile loop visits key tiles of width B_c in ascending order;
+ *     a tile with no visible key for a row is skipped for that row.
+ *   - alpha = 0 while the running max is still -infinity.
+ *   - Causal: key j is visible to query i iff j <= i.
+ */
+#include "oracle.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdatomic.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* E2M1 magnitudes in code order 0..7 [P1 Eq. 9, Eq. 67]. */
+static const double GRID[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double oracle_e2m1_magnitude(int code) { return GRID[code & 7]; }
+
+double oracle_e2m1_value(int code) {
+  double v = GRID[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* Round-to-nearest projection onto the finite grid [P1 Eq. 10].  The nearest
+ * neighbour is decided by comparing with the midpoint of two adjacent grid
+ * points (the decision boundaries of Eq. 68), which is exact in binary64.
+ * Above the last midpoint every value maps to the largest element, 6: this is
+ * the saturation of Eq. 10. */
+int oracle_e2m1_project(double y) {
+  for (int c = 0; c < 7; ++c) {
+    double mid = 0.5 * (GRID[c] + GRID[c + 1]);
+    if (y < mid) return c;
+    if (y == mid) return (c % 2 == 0) ? c : c + 1; /* tie: even code */
+  }
+  return 7;
+}
+
+/* Smallest integer e with M <= q * 2^e, i.e. ceil(log2(M/q)) [P1 Eq. 13].
+ * The frexp estimate is corrected with exact power-of-two comparisons. */
+static int ceil_log2_ratio(double M, double q) {
+  int E;
+  (void)frexp(M / q, &E);
+  int e = E;
+  while (M <= ldexp(q, e - 1)) --e;
+  while (M > ldexp(q, e)) ++e;
+  return e;
+}
+
+/* Largest integer k with q * 2^k <= M, i.e. floor(log2(M/q)). */
+static int floor_log2_ratio(double M, double q) {
+  int E;
+  (void)frexp(M / q, &E);
+  int k = E - 1;
+  while (ldexp(q, k) > M) --k;
+  while (ldexp(q, k + 1) <= M) ++k;
+  return k;
+}
+
+int oracle_scale_exponent(double M, int rule, double q) {
+  switch (rule) {
+    case ORACLE_RULE_UOS: /* UOS boundary q* = 29/4 [P1 Eq. 38-39, Alg. 1] */
+      return ceil_log2_ratio(M, 7.25);
+    case ORACLE_RULE_OCP: /* floor(log2 M) - e_max^elem, e_max^elem = 2 [P1 Eq. 11] */
+      return floor_log2_ratio(M, 1.0) - 2;
+    case ORACLE_RULE_CEIL_Q: /* [P1 Eq. 13] */
+      return ceil_log2_ratio(M, q);
+    case ORACLE_RULE_FLOOR_Q: /* [P1 Eq. 12] */
+      return floor_log2_ratio(M, q) + 1;
+    default:
+      return 0;
+  }
+}
+
+void oracle_scale_exponents(const double* M, int64_t n, int rule, double q, int32_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = oracle_scale_exponent(M[i], rule, q);
+}
+
+/* [P1 Alg. 1]: block max M; an all-zero block gets sigma = 1 and zero
+ * elements; otherwise sigma = 2^e from the rule, and each element is
+ * sigma * Pi(v / sigma). */
+int oracle_quantize_block(const double* x, int n, int rule, double q,
+                          uint8_t* scale_byte, uint8_t* codes) {
+  double M = 0.0;
+  for (int i = 0; i < n; ++i)
+    if (fabs(x[i]) > M) M = fabs(x[i]);
+  int e = 0;
+  if (M > 0.0) {
+    e = oracle_scale_exponent(M, rule, q);
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+  }
+  *scale_byte = (uint8_t)(e + 127);
+  for (int i = 0; i < n; ++i) {
+    int c = oracle_e2m1_project(ldexp(fabs(x[i]), -e));
+    codes[i] = (uint8_t)(c | (signbit(x[i]) ? 8 : 0));
+  }
+  return e;
+}
+
+static double dequant(uint8_t code, uint8_t scale_byte) {
+  return ldexp(oracle_e2m1_value(code), (int)scale_byte - 127);
+}
+
+float oracle_decode_half(uint16_t bits, int dtype) {
+  if (dtype == ORACLE_BF16) {
+    uint32_t u = (uint32_t)bits << 16; /* bfloat16 is the top half of binary32 */
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+  }
+  /* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits */
+  int s = bits >> 15, E = (bits >> 10) & 31, F = bits & 1023;
+  double v;
+  if (E == 0) v = ldexp((double)F, -24);
+  else if (E == 31) v = F ? NAN : INFINITY;
+  else v = ldexp((double)(F + 1024), E - 25);
+  return (float)(s ? -v : v);
+}
+
+void oracle_hadamard_rotate_f32(float* x, int d) {
+  for (int h = 1; h < d; h <<= 1)
+    for (int i = 0; i < d; ++i)
+      if ((i & h) == 0) {
+        float a = x[i], b = x[i + h];
+        x[i] = a + b;
+        x[i + h] = a - b;
+      }
+  const float r = (float)(1.0 / sqrt((double)d));
+  for (int i = 0; i < d; ++i) x[i] = x[i] * r;
+}
+
+/* ------------------------------------------------------------------ */
+/* small thread pool: workers pull item indices from an atomic counter  */
+
+typedef void (*item_fn)(void* ctx, int64_t item, void* scratch);
+
+typedef struct {
+  item_fn fn;
+  void* ctx;
+  int64_t n_items;
+  size_t scratch_bytes;
+  atomic_llong next;
+  atomic_int failed;
+} pool_t;
+
+static void* pool_worker(void* arg) {
+  pool_t* p = (pool_t*)arg;
+  void* scratch = p->scratch_bytes ? malloc(p->scratch_bytes) : NULL;
+  if (p->scratch_bytes && !scratch) {
+    atomic_store(&p->failed, 1);
+    return NULL;
+  }
+  for (;;) {
+    int64_t it = atomic_fetch_add(&p->next, 1);
+    if (it >= p->n_items) break;
+    p->fn(p->ctx, it, scratch);
+  }
+  free(scratch);
+  return NULL;
+}
+
+static int run_pool(item_fn fn, void* ctx, int64_t n_items, size_t scratch_bytes, int nthreads) {
+  pool_t p;
+  p.fn = fn;
+  p.ctx = ctx;
+  p.n_items = n_items;
+  p.scratch_bytes = scratch_bytes;
+  atomic_init(&p.next, 0);
+  atomic_init(&p.failed, 0);
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > n_items) nthreads = (int)(n_items > 0 ? n_items : 1);
+  pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
+  if (!th) return -1;
+  int started = 0;
+  for (int t = 0; t < nthreads; ++t)
+    if (pthread_create(&th[t], NULL, pool_worker, &p) == 0) ++started;
+  if (started == 0) pool_worker(&p);
+  for (int t = 0; t < started; ++t) pthread_join(th[t], NULL);
+  free(th);
+  return atomic_load(&p.failed) ? -1 : 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* tensor quantization                                                  */
+
+typedef struct {
+  const uint16_t* x;
+  int dtype, B, H, N, d, rotate, rule;
+  double q;
+  int64_t sB, sH, sN;
+  const int64_t* rows;
+  uint8_t* codes;
+  uint8_t* scales;
+} qrows_ctx;
+
+static void strides_or_contig(const int64_t* strides, int H, int N, int d, int64_t* sB, int64_t* sH,
+                              int64_t* sN) {
+  if (strides) {
+    *sB = strides[0];
+    *sH = strides[1];
+    *sN = strides[2];
+  } else {
+    *sN = d;
+    *sH = (int64_t)N * d;
+    *sB = (int64_t)H * N * d;
+  }
+}
+
+/* One Q/K row: decode, optionally rotate (binary32), then quantize each
+ * 32-channel block along the head dimension [P1 Alg. 2 steps 3-6]. */
+static void quantize_row(const qrows_ctx* c, int64_t g, uint8_t* codes, uint8_t* scales, float* buf) {
+  int64_t bh = g / c->N, n = g % c->N;
+  int64_t b = bh / c->H, h = bh % c->H;
+  const uint16_t* src = c->x + b * c->sB + h * c->sH + n * c->sN;
+  for (int i = 0; i < c->d; ++i) buf[i] = oracle_decode_half(src[i], c->dtype);
+  if (c->rotate) oracle_hadamard_rotate_f32(buf, c->d);
+  double blk[32];
+  for (int k = 0; k < c->d / 32; ++k) {
+    for (int i = 0; i < 32; ++i) blk[i] = (double)buf[32 * k + i];
+    oracle_quantize_block(blk, 32, c->rule, c->q, &scales[k], &codes[32 * k]);
+  }
+}
+
+static void qrows_item(void* ctx, int64_t it, void* scratch) {
+  const qrows_ctx* c = (const qrows_ctx*)ctx;
+  int64_t g = c->rows ? c->rows[it] : it;
+  quantize_row(c, g, c->codes + it * c->d, c->scales + it * (c->d / 32), (float*)scratch);
+}
+
+static int shape_ok(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 32) return 0;
+  if ((d & (d - 1)) != 0) return 0; /* the Sylvester construction needs a power of two */
+  return 1;
+}
+
+int oracle_quantize_rows(const uint16_t* x, int dtype, int B, int H, int N, int d,
+                         const int64_t* strides, int rotate, int rule, double q,
+                         const int64_t* rows, int64_t n_rows,
+                         uint8_t* codes, uint8_t* scales, int nthreads) {
+  if (!x || !codes || !scales || !shape_ok(B, H, N, d) || n_rows < 0) return -1;
+  qrows_ctx c = {x, dtype, B, H, N, d, rotate, rule, q, 0, 0, 0, rows, codes, scales};
+  strides_or_contig(strides, H, N, d, &c.sB, &c.sH, &c.sN);
+  if (rows)
+    for (int64_t r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= (int64_t)B * H * N) return -1;
+  return run_pool(qrows_item, &c, n_rows, sizeof(float) * (size_t)d, nthreads);
+}
+
+typedef struct {
+  const uint16_t* x;
+  int dtype, B, H, N, d, rule;
+  double q;
+  int64_t sB, sH, sN, NB;
+  const int64_t* blocks;
+  uint8_t* codes;
+  uint8_t* scales;
+} qblk_ctx;
+
+/* One V token block: for every channel, the 32 tokens 32*kb..32*kb+31
+ * (+0 past the end) form one MXFP4 block [P3, Quantizing attention]. */
+static void qblk_item(void* ctx, int64_t it, void* scratch) {
+  (void)scratch;
+  const qblk_ctx* c = (const qblk_ctx*)ctx;
+  int64_t gb = c->blocks ? c->blocks[it] : it;
+  int64_t bh = gb / c->NB, kb = gb % c->NB;
+  int64_t b = bh / c->H, h = bh % c->H;
+  const uint16_t* base = c->x + b * c->sB + h * c->sH;
+  double blk[32];
+  for (int ch = 0; ch < c->d; ++ch) {
+    for (int t = 0; t < 32; ++t) {
+      int64_t n = 32 * kb + t;
+      blk[t] = n < c->N ? (double)oracle_decode_half(base[n * c->sN + ch], c->dtype) : 0.0;
+    }
+    oracle_quantize_block(blk, 32, c->rule, c->q, &c->scales[it * c->d + ch],
+                          &c->codes[(it * c->d + ch) * 32]);
+  }
+}
+
+int oracle_quantize_token_blocks(const uint16_t* x, int dtype, int B, int H, int N, int d,
+                                 const int64_t* strides, int rule, double q,
+                                 const int64_t* blocks, int64_t n_blocks,
+                                 uint8_t* codes, uint8_t* scales, int nthreads) {
+  if (!x || !codes || !scales || !shape_ok(B, H, N, d) || n_blocks < 0) return -1;
+  qblk_ctx c = {x, dtype, B, H, N, d, rule, q, 0, 0, 0, (N + 31) / 32, blocks, codes, scales};
+  strides_or_contig(strides, H, N, d, &c.sB, &c.sH, &c.sN);
+  if (blocks)
+    for (int64_t r = 0; r < n_blocks; ++r)
+      if (blocks[r] < 0 || blocks[r] >= (int64_t)B * H * c.NB) return -1;
+  return run_pool(qblk_item, &c, n_blocks, 0, nthreads);
+}
+
+/* ------------------------------------------------------------------ */
+/* attention                                                            */
+
+typedef struct {
+  const oracle_attn_cfg* cfg;
+  const uint16_t *q, *k, *v;
+  int64_t sB, sH, sN;
+  const int32_t* rows;
+  int32_t n_rows;
+  int32_t chunks_per_head, rows_per_chunk;
+  double *out, *m_out, *l_out, *rowsum, *amb;
+} attn_ctx;
+
+/* Dequantized (or plain) K and V of one head, and the query row, in binary64. */
+static void load_head_kv(const attn_ctx* c, int64_t b, int64_t h, double* K, double* V, float* buf,
+                         uint8_t* codes, double* blk) {
+  const oracle_attn_cfg* g = c->cfg;
+  const int N = g->N, d = g->d;
+  const uint16_t* kb = c->k + b * c->sB + h * c->sH;
+  const uint16_t* vb = c->v + b * c->sB + h * c->sH;
+  for (int j = 0; j < N; ++j) {
+    for (int i = 0; i < d; ++i) buf[i] = oracle_decode_half(kb[(int64_t)j * c->sN + i], g->dtype);
+    if (g->rotate) oracle_hadamard_rotate_f32(buf, d);
+    if (g->quant) {
+      for (int kk = 0; kk < d / 32; ++kk) {
+        uint8_t sb;
+        for (int i = 0; i < 32; ++i) blk[i] = (double)buf[32 * kk + i];
+        oracle_quantize_block(blk, 32, g->rule, g->q, &sb, codes);
+        for (int i = 0; i < 32; ++i) K[(int64_t)j * d + 32 * kk + i] = dequant(codes[i], sb);
+      }
+    } else {
+      for (int i = 0; i < d; ++i) K[(int64_t)j * d + i] = (double)buf[i];
+    }
+  }
+  if (g->quant) {
+    /* V along tokens, 32-token blocks aligned to token 0, +0 padding [P3] */
+    for (int kb32 = 0; kb32 < (N + 31) / 32; ++kb32)
+      for (int ch = 0; ch < d; ++ch) {
+        uint8_t sb;
+        for (int t = 0; t < 32; ++t) {
+          int n = 32 * kb32 + t;
+          blk[t] = n < N ? (double)oracle_decode_half(vb[(int64_t)n * c->sN + ch], g->dtype) : 0.0;
+        }
+        oracle_quantize_block(blk, 32, g->rule, g->q, &sb, codes);
+        for (int t = 0; t < 32; ++t) {
+          int n = 32 * kb32 + t;
+          if (n < N) V[(int64_t)n * d + ch] = dequant(codes[t], sb);
+        }
+      }
+  } else {
+    for (int j = 0; j < N; ++j)
+      for (int ch = 0; ch < d; ++ch)
+        V[(int64_t)j * d + ch] = (double)oracle_decode_half(vb[(int64_t)j * c->sN + ch], g->dtype);
+  }
+}
+
+static void load_query(const attn_ctx* c, int64_t b, int64_t h, int i, double* qv, float* buf,
+                       uint8_t* codes, double* blk) {
+  const oracle_attn_cfg* g = c->cfg;
+  const int d = g->d;
+  const uint16_t* src = c->q + b * c->sB + h * c->sH + (int64_t)i * c->sN;
+  for (int t = 0; t < d; ++t) buf[t] = oracle_decode_half(src[t], g->dtype);
+  if (g->rotate) oracle_hadamard_rotate_f32(buf, d);
+  if (g->quant) {
+    for (int kk = 0; kk < d / 32; ++kk) {
+      uint8_t sb;
+      for (int t = 0; t < 32; ++t) blk[t] = (double)buf[32 * kk + t];
+      oracle_quantize_block(blk, 32, g->rule, g->q, &sb, codes);
+      for (int t = 0; t < 32; ++t) qv[32 * kk + t] = dequant(codes[t], sb);
+    }
+  } else {
+    for (int t = 0; t < d; ++t) qv[t] = (double)buf[t];
+  }
+}
+
+/* Quantize one 32-key block of exponentials p[0..31] (a tile segment, zeros
+ * for keys that are masked or past N) and return the dequantized values in
+ * ph.  If delta > 0, also write into dp the largest change of each element
+ * that a decision within relative margin delta of its boundary could make:
+ * an element lying near a rounding midpoint may round to the neighbouring
+ * grid point, and a block maximum lying near a scale boundary may select the
+ * neighbouring exponent (the whole block is then re-projected). */
+static void quantize_p_block(const oracle_attn_cfg* g, const double* p, double* ph, double* dp) {
+  uint8_t codes[32], sb;
+  int e = oracle_quantize_block(p, 32, g->rule, g->q, &sb, codes);
+  for (int t = 0; t < 32; ++t) ph[t] = dequant(codes[t], sb);
+  if (!dp) return;
+  const double delta = g->amb_delta;
+  for (int t = 0; t < 32; ++t) {
+    dp[t] = 0.0;
+    double y = ldexp(p[t], -e);
+    for (int c = 0; c < 7; ++c) {
+      double mid = 0.5 * (GRID[c] + GRID[c + 1]);
+      if (fabs(y - mid) <= delta * mid) {
+        double step = ldexp(GRID[c + 1] - GRID[c], e);
+        if (step > dp[t]) dp[t] = step;
+      }
+    }
+  }
+  double M = 0.0;
+  for (int t = 0; t < 32; ++t)
+    if (p[t] > M) M = p[t];
+  if (M <= 0.0) return;
+  /* normalized block max and the two ends of its admissible interval */
+  double r = ldexp(M, -e), hi, lo;
+  switch (g->rule) {
+    case ORACLE_RULE_UOS: hi = 7.25; lo = 3.625; break;
+    case ORACLE_RULE_CEIL_Q: hi = g->q; lo = 0.5 * g->q; break;
+    case ORACLE_RULE_OCP: hi = 8.0; lo = 4.0; break;
+    default: hi = g->q; lo = 0.5 * g->q; break;
+  }
+  int alts[2], na = 0;
+  if (fabs(r - hi) <= delta * hi && e < 127) alts[na++] = e + 1;
+  if (fabs(r - lo) <= delta * lo && e > -127) alts[na++] = e - 1;
+  for (int a = 0; a < na; ++a) {
+    int ea = alts[a];
+    for (int t = 0; t < 32; ++t) {
+      double alt = ldexp(GRID[oracle_e2m1_project(ldexp(p[t], -ea))], ea);
+      double diff = fabs(alt - ph[t]);
+      if (diff > dp[t]) dp[t] = diff;
+    }
+  }
+}
+
+static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
+  const attn_ctx* c = (const attn_ctx*)vctx;
+  const oracle_attn_cfg* g = c->cfg;
+  const int N = g->N, d = g->d, Bc = g->kv_tile;
+  const int T = (N + Bc - 1) / Bc;
+  const int64_t bh = item / c->chunks_per_head;
+  const int chunk = (int)(item % c->chunks_per_head);
+  const int64_t b = bh / g->H, h = bh % g->H;
+  int r0 = chunk * c->rows_per_chunk, r1 = r0 + c->rows_per_chunk;
+  if (r1 > c->n_rows) r1 = c->n_rows;
+  if (r0 >= r1) return;
+
+  /* scratch layout */
+  char* s = (char*)scratch_raw;
+  double* K = (double*)s;  s += sizeof(double) * (size_t)N * d;
+  double* V = (double*)s;  s += sizeof(double) * (size_t)N * d;
+  double* qv = (double*)s; s += sizeof(double) * d;
+  double* o = (double*)s;  s += sizeof(double) * d;
+  double* ao = (double*)s; s += sizeof(double) * d;
+  double* sc = (double*)s; s += sizeof(double) * (size_t)N;   /* scores of the row  */
+  double* pt = (double*)s; s += sizeof(double) * (size_t)(T * Bc); /* P~ (tile-padded) */
+  double* ph = (double*)s; s += sizeof(double) * (size_t)(T * Bc); /* P^              */
+  double* dp = (double*)s; s += sizeof(double) * (size_t)(T * Bc); /* allowance       */
+  double* tm = (double*)s; s += sizeof(double) * T;  /* m after tile t           */
+  double* th = (double*)s; s += sizeof(double) * T;  /* sum of P^ over tile t    */
+  double* tt = (double*)s; s += sizeof(double) * T;  /* sum of P~ over tile t    */
+  double* blk = (double*)s; s += sizeof(double) * 32;
+  float* buf = (float*)s;  s += sizeof(float) * d;
+  uint8_t* codes = (uint8_t*)s;
+
+  load_head_kv(c, b, h, K, V, buf, codes, blk);
+
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+  const int quantize_p = g->quant && g->p_mode != ORACLE_P_EXACT;
+  const int want_amb = c->amb && quantize_p && g->amb_delta > 0.0;
+
+  for (int r = r0; r < r1; ++r) {
+    const int i = c->rows ? c->rows[r] : r;
+    load_query(c, b, h, i, qv, buf, codes, blk);
+    const int jvis = g->causal ? (i + 1 < N ? i + 1 : N) : N; /* keys [0, jvis) visible */
+    /* S_ij = q^ . k^_j / sqrt(d) [P1 Eq. 2, Alg. 2 step 11] */
+    for (int j = 0; j < jvis; ++j) {
+      double acc = 0.0;
+      for (int t = 0; t < d; ++t) acc += qv[t] * K[(int64_t)j * d + t];
+      sc[j] = acc * inv_sqrt_d;
+    }
+    double* orow = c->out + (bh * c->n_rows + r) * d;
+    double* arow = c->amb ? c->amb + (bh * c->n_rows + r) * d : NULL;
+    const int64_t ridx = bh * c->n_rows + r;
+    for (int t = 0; t < d; ++t) { o[t] = 0.0; ao[t] = 0.0; }
+
+    if (g->p_mode == ORACLE_P_POSTNORM && g->quant) {
+      /* Materialized-P diagnostic [P1 Sec. 5.5.2]: exact softmax first, then
+       * quantize the normalized probabilities in aligned 32-key blocks and
+       * accumulate O = Q(P) V^ with no renormalization. */
+      double ms = -INFINITY, ls = 0.0;
+      for (int j = 0; j < jvis; ++j) if (sc[j] > ms) ms = sc[j];
+      for (int j = 0; j < jvis; ++j) ls += exp(sc[j] - ms);
+      double sum_hat = 0.0;
+      for (int j0 = 0; j0 < jvis; j0 += 32) {
+        double pb[32], hb[32], db[32];
+        for (int t = 0; t < 32; ++t) pb[t] = (j0 + t < jvis) ? exp(sc[j0 + t] - ms) / ls : 0.0;
+        quantize_p_block(g, pb, hb, want_amb ? db : NULL);
+        for (int t = 0; t < 32 && j0 + t < jvis; ++t) {
+          sum_hat += hb[t];
+          for (int ch = 0; ch < d; ++ch) o[ch] += hb[t] * V[(int64_t)(j0 + t) * d + ch];
+          if (want_amb)
+            for (int ch = 0; ch < d; ++ch) ao[ch] += db[t] * fabs(V[(int64_t)(j0 + t) * d + ch]);
+        }
+      }
+      for (int ch = 0; ch < d; ++ch) orow[ch] = o[ch];
+      if (arow) for (int ch = 0; ch < d; ++ch) arow[ch] = want_amb ? ao[ch] : 0.0;
+      if (c->m_out) c->m_out[ridx] = ms;
+      if (c->l_out) c->l_out[ridx] = ls;
+      if (c->rowsum) c->rowsum[ridx] = sum_hat;
+      continue;
+    }
+
+    /* Online softmax over key tiles in ascending order [P1 Alg. 2 steps 9-19;
+     * Eqs. 3-7 with Eqs. 44-48 (PNQ) or Eq. 42 (direct)]. */
+    double m = -INFINITY, l = 0.0, al = 0.0;
+    int ntiles_seen = 0;
+    for (int tile = 0; tile < T; ++tile) {
+      const int j0 = tile * Bc;
+      int j1 = j0 + Bc < jvis ? j0 + Bc : jvis;
+      tm[tile] = -INFINITY; th[tile] = 0.0; tt[tile] = 0.0;
+      if (j1 <= j0) continue; /* no visible key for this row: a no-op */
+      ++ntiles_seen;
+      double smax = -INFINITY;
+      for (int j = j0; j < j1; ++j) if (sc[j] > smax) smax = sc[j];
+      const double m_new = m > smax ? m : smax;                 /* Eq. 3  */
+      const double alpha = (m == -INFINITY) ? 0.0 : exp(m - m_new); /* Eq. 4 */
+      double* P = pt + j0;
+      double* Ph = ph + j0;
+      double* D = dp + j0;
+      for (int t = 0; t < Bc; ++t) P[t] = (j0 + t < j1) ? exp(sc[j0 + t] - m_new) : 0.0; /* Eq. 5 */
+      for (int t0 = 0; t0 < Bc; t0 += 32) {
+        if (quantize_p) quantize_p_block(g, P + t0, Ph + t0, want_amb ? D + t0 : NULL); /* Eq. 44 */
+        else for (int t = 0; t < 32; ++t) Ph[t0 + t] = P[t0 + t];
+      }
+      double sum_hat = 0.0, sum_til = 0.0;
+      for (int t = 0; t < Bc; ++t) { sum_hat += Ph[t]; sum_til += P[t]; }
+      /* l update: Eq. 47 (PNQ) or Eq. 16 / Eq. 42 (direct) */
+      l = alpha * l + ((g->p_mode == ORACLE_P_DIRECT && quantize_p) ? sum_til : sum_hat);
+      /* O update: Eq. 48 / Eq. 17 */
+      for (int ch = 0; ch < d; ++ch) o[ch] *= alpha;
+      for (int j = j0; j < j1; ++j) {
+        const double w = Ph[j - j0];
+        if (w != 0.0)
+          for (int ch = 0; ch < d; ++ch) o[ch] += w * V[(int64_t)j * d + ch];
+      }
+      if (want_amb) {
+        double dl = 0.0;
+        for (int ch = 0; ch < d; ++ch) ao[ch] *= alpha;
+        for (int j = j0; j < j1; ++j) {
+          const double w = D[j - j0];
+          if (w != 0.0) {
+            dl += w;
+            for (int ch = 0; ch < d; ++ch) ao[ch] += w * fabs(V[(int64_t)j * d + ch]);
+          }
+        }
+        al = alpha * al + dl;
+      }
+      tm[tile] = m_new; th[tile] = sum_hat; tt[tile] = sum_til;
+      m = m_new;                                                /* step 18 */
+    }
+    (void)ntiles_seen;
+    /* O_i = o / l  [Eq. 8; Alg. 2 step 20]; POSTNORM without quantization
+     * reduces to the same exact softmax attention. */
+    for (int ch = 0; ch < d; ++ch) orow[ch] = o[ch] / l;
+    if (arow) {
+      for (int ch = 0; ch < d; ++ch) {
+        if (!want_amb) arow[ch] = 0.0;
+        else if (g->p_mode == ORACLE_P_DIRECT) arow[ch] = ao[ch] / l;
+        else arow[ch] = (l > al) ? (ao[ch] + fabs(orow[ch]) * al) / (l - al) : INFINITY;
+      }
+    }
+    if (c->m_out) c->m_out[ridx] = m;
+    if (c->l_out) c->l_out[ridx] = l;
+    if (c->rowsum) {
+      /* effective full-row form: beta_t = exp(m_t - m_final) [App. H Eq. 99] */
+      double num = 0.0, den = 0.0;
+      for (int tile = 0; tile < T; ++tile) {
+        if (tm[tile] == -INFINITY) continue;
+        const double beta = exp(tm[tile] - m);
+        num += beta * th[tile];
+        den += beta * tt[tile];
+      }
+      if (g->p_mode == ORACLE_P_DIRECT && quantize_p) c->rowsum[ridx] = num / den; /* Eq. 110 */
+      else c->rowsum[ridx] = num / l;                                              /* Eq. 51  */
+    }
+  }
+}
+
+int oracle_attention(const oracle_attn_cfg* cfg,
+                     const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                     const int64_t* strides, const int32_t* rows, int32_t n_rows,
+                     double* out, double* m_out, double* l_out, double* rowsum,
+                     double* amb) {
+  if (!cfg || !q || !k || !v || !out) return -1;
+  if (!shape_ok(cfg->B, cfg->H, cfg->N, cfg->d)) return -1;
+  if (cfg->kv_tile < 32 || cfg->kv_tile % 32 != 0) return -1;
+  if (cfg->p_mode < 0 || cfg->p_mode > 3) return -1;
+  if (!rows) n_rows = cfg->N;
+  if (n_rows < 1) return -1;
+  if (rows)
+    for (int r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= cfg->N) return -1;
+  attn_ctx c;
+  memset(&c, 0, sizeof c);
+  c.cfg = cfg;
+  c.q = q; c.k = k; c.v = v;
+  strides_or_contig(strides, cfg->H, cfg->N, cfg->d, &c.sB, &c.sH, &c.sN);
+  c.rows = rows;
+  c.n_rows = n_rows;
+  c.out = out; c.m_out = m_out; c.l_out = l_out; c.rowsum = rowsum; c.amb = amb;
+  const int64_t heads = (int64_t)cfg->B * cfg->H;
+  int nth = cfg->nthreads > 0 ? cfg->nthreads : 1;
+  int cph = (int)((2 * (int64_t)nth + heads - 1) / heads);
+  if (cph < 1) cph = 1;
+  if (cph > n_rows) cph = n_rows;
+  c.chunks_per_head = cph;
+  c.rows_per_chunk = (n_rows + cph - 1) / cph;
+  const int N = cfg->N, d = cfg->d, T = (N + cfg->kv_tile - 1) / cfg->kv_tile;
+  size_t scratch = sizeof(double) * ((size_t)2 * N * d + 3 * (size_t)d + N + 3 * (size_t)T * cfg->kv_tile +
+                                     3 * (size_t)T + 32) +
+                   sizeof(float) * d + 64;
+  return run_pool(attn_item, &c, heads * cph, scratch, nth);
+}

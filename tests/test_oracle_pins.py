@@ -1,0 +1,631 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test states the passage it checks.  None of them re-derives a value from
+the oracle's own formula: the references are the pages' printed values and
+closed forms, textbook identities, library routines (numpy, scipy) and brute
+force over small inputs.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def golden_lines(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.split() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+def grid_from_golden():
+    rows = {r[0]: [Fraction(x) for x in r[1:]] for r in golden_lines("e2m1_grid.txt")}
+    return rows["grid"], rows["boundaries"]
+
+
+# --------------------------------------------------------------------------
+# E2M1 element format  [P1 Sec. 2 Eqs. 9-10; App. B Eqs. 67-68]
+
+
+def test_grid_matches_page():
+    grid, _ = grid_from_golden()
+    assert [Fraction(oracle.e2m1_magnitude(c)) for c in range(8)] == grid
+    for c in range(8):
+        assert oracle.e2m1_value(c | 8) == -oracle.e2m1_magnitude(c)
+
+
+def test_projection_is_nearest_grid_point_brute_force():
+    """Every dyadic y on a 1/128 lattice in [0, 9] plus random y: the returned
+    grid value is a nearest one (exact rational distances), ties go to the
+    even code, and everything beyond the grid saturates at 6 [Eq. 10]."""
+    grid, _ = grid_from_golden()
+    rng = np.random.default_rng(7)
+    ys = [Fraction(k, 128) for k in range(0, 9 * 128 + 1)]
+    ys += [Fraction(float(y)) for y in rng.uniform(0, 12, 4000)]
+    for y in ys:
+        c = oracle.e2m1_project(float(y))
+        dists = [abs(y - g) for g in grid]
+        best = min(dists)
+        assert dists[c] == best, (y, c)
+        nearest = [i for i, dd in enumerate(dists) if dd == best]
+        if len(nearest) == 2:
+            assert c % 2 == 0, (y, c)
+
+
+def test_decision_boundaries_and_ties_match_page():
+    """The code changes exactly at the printed boundaries [Eq. 68] and the
+    value at each boundary goes to the even code."""
+    _, bounds = grid_from_golden()
+    for k, t in enumerate(bounds):
+        t = float(t)
+        below = oracle.e2m1_project(math.nextafter(t, 0.0))
+        above = oracle.e2m1_project(math.nextafter(t, 100.0))
+        assert (below, above) == (k, k + 1)
+        at = oracle.e2m1_project(t)
+        assert at in (k, k + 1) and at % 2 == 0
+    for y in (5.000001, 6.0, 7.0, 7.25, 8.0, 1e30):
+        assert oracle.e2m1_project(y) == 7
+
+
+def test_sign_and_zero_blocks():
+    # all-zero block: sigma = 1 and every element 0 [P1 Sec. 2 end; Alg. 1 steps 4-7]
+    sb, codes, e = oracle.quantize_block(np.zeros(32))
+    assert sb == 127 and e == 0 and not codes.any()
+    # negative zero keeps its sign bit (reading of the pages' silence on signed zero)
+    sb, codes, _ = oracle.quantize_block(np.full(32, -0.0))
+    assert sb == 127 and (codes == 8).all()
+    x = np.zeros(32)
+    x[0], x[1], x[2] = 12.0, -0.001, -3.0  # e = ceil(log2(12/7.25)) = 1
+    sb, codes, e = oracle.quantize_block(x)
+    assert e == 1 and sb == 128 and codes[0] == 7 and codes[1] == 8 and codes[2] == 0x8 | 3
+
+
+# --------------------------------------------------------------------------
+# shared-scale rules  [P1 Sec. 2 Eqs. 11-13; Sec. 4.1 Eq. 19, Alg. 1; P2]
+
+
+def test_uos_worked_examples():
+    for M, e, scale, xnorm in golden_lines("uos_worked_examples.txt"):
+        M, e, scale, xnorm = float(M), int(e), float(scale), float(xnorm)
+        assert oracle.scale_exponent(M, oracle.RULE_UOS) == e
+        assert 2.0 ** e == scale and M / scale == xnorm
+        blk = np.zeros(32)
+        blk[5] = M
+        sb, codes, ee = oracle.quantize_block(blk)
+        assert ee == e and sb == e + 127
+        # dequantized block maximum: Q*(14.5) = 2 * Pi(7.25) = 12 (saturation at 6),
+        # Q*(1) = (1/4) * 4 = 1 exactly [App. J Eq. 117]
+        deq = oracle.e2m1_value(codes[5]) * scale
+        assert deq == {14.5: 12.0, 1.0: 1.0}[M]
+
+
+def _positive_bf16():
+    bits = np.arange(1, 0x7F80, dtype=np.uint32)  # every positive finite bfloat16
+    return (bits << 16).view(np.float32).astype(np.float64)
+
+
+def test_normalized_max_ranges_exhaustive_bf16_and_random_fp32():
+    """UOS maps the block maximum into (3.625, 7.25] [Alg. 1 range statement],
+    OCP into [4, 8) [Eq. 11, Sec. 3], e_ceil(q) into (q/2, q] [Eq. 19],
+    e_floor(q) into [q/2, q) [Eq. 12]."""
+    rng = np.random.default_rng(11)
+    rnd32 = (rng.integers(0x00800000, 0x7F800000, 200000, dtype=np.uint32)).view(np.float32)
+    for M in (_positive_bf16(), rnd32.astype(np.float64)):
+        eu = oracle.scale_exponents(M, oracle.RULE_UOS).astype(np.float64)
+        eo = oracle.scale_exponents(M, oracle.RULE_OCP).astype(np.float64)
+        xu, xo = M / np.exp2(eu), M / np.exp2(eo)
+        assert ((xu > 3.625) & (xu <= 7.25)).all()
+        assert ((xo >= 4.0) & (xo < 8.0)).all()
+        # UOS differs from OCP by at most one binade, exactly when the OCP-normalized
+        # maximum lies above 7.25 (difference of Eqs. 11 and 13 with q = 7.25)
+        diff = eu - eo
+        assert set(np.unique(diff)) <= {0.0, 1.0}
+        assert ((diff == 1.0) == (xo > 7.25)).all()
+        for q in (6.0, 7.0, 7.25, 8.0, 6.05):
+            ec = oracle.scale_exponents(M, oracle.RULE_CEIL_Q, q).astype(np.float64)
+            ef = oracle.scale_exponents(M, oracle.RULE_FLOOR_Q, q).astype(np.float64)
+            xc, xf = M / np.exp2(ec), M / np.exp2(ef)
+            assert ((xc > q / 2) & (xc <= q)).all()
+            assert ((xf >= q / 2) & (xf < q)).all()
+            # floor and ceiling forms differ only where M/q is a power of two [Sec. 2]
+            ratio = M / q
+            pow2 = (np.frexp(ratio)[0] == 0.5)
+            assert ((ec != ef) == pow2).all()
+
+
+def test_oas_equivalent_rule_relation():
+    """App. G, Eq. 96: e_7 = e_6 - 1 when x_6 in (3, 3.5], else e_6."""
+    M = _positive_bf16()
+    e6 = oracle.scale_exponents(M, oracle.RULE_CEIL_Q, 6.0)
+    e7 = oracle.scale_exponents(M, oracle.RULE_CEIL_Q, 7.0)
+    x6 = M / np.exp2(e6.astype(np.float64))
+    expect = np.where((x6 > 3.0) & (x6 <= 3.5), e6 - 1, e6)
+    assert (e7 == expect).all()
+
+
+def test_e8m0_clamp():
+    # M = 2^-126 would need e = -128 under UOS; the E8M0 byte clamps at 2^-127
+    M = 2.0 ** -126
+    assert oracle.scale_exponent(M, oracle.RULE_UOS) == -128
+    blk = np.zeros(32)
+    blk[0] = M
+    sb, codes, e = oracle.quantize_block(blk)
+    assert sb == 0 and e == -127 and codes[0] == 4  # 2^-126 / 2^-127 = 2 -> code 4
+
+
+# --------------------------------------------------------------------------
+# closed forms of the error analysis, from the *implemented* projection
+# [P1 Sec. 4.1 Eqs. 21, 35-39; App. B Eqs. 69-73; App. C Eq. 81]
+
+
+def implemented_pieces():
+    """Piecewise-constant map of oracle.e2m1_project on [0, inf): boundaries
+    located by bisection between lattice points where the code changes."""
+    lattice = [k / 64.0 for k in range(0, 64 * 10 + 1)]
+    codes = [oracle.e2m1_project(x) for x in lattice]
+    cuts = []
+    for a, b, ca, cb in zip(lattice, lattice[1:], codes, codes[1:]):
+        if ca == cb:
+            continue
+        lo, hi = a, b
+        while math.nextafter(lo, hi) < hi:
+            mid = 0.5 * (lo + hi)
+            if oracle.e2m1_project(mid) == ca:
+                lo = mid
+            else:
+                hi = mid
+        cuts.append((Fraction(hi).limit_denominator(1 << 20), ca, cb))
+    pieces, start = [], Fraction(0)
+    for t, ca, _ in cuts:
+        pieces.append((start, t, Fraction(oracle.e2m1_magnitude(ca))))
+        start = t
+    pieces.append((start, Fraction(10 ** 9), Fraction(oracle.e2m1_magnitude(cuts[-1][2]))))
+    return pieces
+
+
+PIECES = None
+
+
+def pieces():
+    global PIECES
+    if PIECES is None:
+        PIECES = implemented_pieces()
+    return PIECES
+
+
+def E_exact(x):
+    """E(x) = int_0^x (v - Pi(v))^2 dv, integrated exactly per piece [Eq. 69]."""
+    x = Fraction(x)
+    total = Fraction(0)
+    for a, b, r in pieces():
+        if a >= x:
+            break
+        bb = min(b, x)
+        total += ((bb - r) ** 3 - (a - r) ** 3) / 3
+    return total
+
+
+def Delta(q):
+    q = Fraction(q)
+    return E_exact(q) - 8 * E_exact(q / 2)
+
+
+def test_implemented_boundaries_are_the_printed_ones():
+    _, bounds = grid_from_golden()
+    assert [a for a, _, _ in pieces()[1:]] == bounds
+
+
+def test_error_integral_closed_forms():
+    rows = golden_lines("closed_forms.txt")
+    for r in rows:
+        if r[0] == "E":
+            assert E_exact(Fraction(r[1])) == Fraction(r[2])
+    # Eq. 70 for q >= 6 and E(29/4) = 7/8 + (5/4)^3/3 = 293/192
+    assert E_exact(Fraction(29, 4)) == Fraction(293, 192)
+    for q in (Fraction(6), Fraction(13, 2), Fraction(9), Fraction(25, 2)):
+        assert E_exact(q) == Fraction(7, 8) + (q - 6) ** 3 / 3
+
+
+def test_delta_pieces_root_and_sign():
+    rows = {r[0]: r[1:] for r in golden_lines("closed_forms.txt")}
+    for q in (Fraction(6), Fraction(25, 4), Fraction(13, 2), Fraction(27, 4), Fraction(7)):
+        assert Delta(q) == Fraction(rows["delta_6_7"][0])
+    for q in (Fraction(7), Fraction(57, 8), Fraction(29, 4), Fraction(15, 2), Fraction(31, 4), Fraction(8)):
+        assert Delta(q) == (4 * q - 29) * (4 * q - 27) / 8
+    root = Fraction(rows["root"][0])
+    assert Delta(root) == 0
+    # sign pattern of Eq. 81
+    for q in (Fraction(1, 16), Fraction(1, 8), Fraction(1, 4)):
+        assert Delta(q) == 0
+    for q in (Fraction(1, 4) + Fraction(1, 1024), Fraction(1), Fraction(3), Fraction(29, 4) - Fraction(1, 1000)):
+        assert Delta(q) < 0
+    for q in (Fraction(29, 4) + Fraction(1, 1000), Fraction(8), Fraction(11), Fraction(100)):
+        assert Delta(q) > 0
+
+
+def test_delta_last_piece_discriminant():
+    """For q >= 12 both E(q) and E(q/2) are on the saturated branch, and 8*Delta
+    is a quadratic whose discriminant the page prints as -18240 [App. C]."""
+    qs = [Fraction(12), Fraction(13), Fraction(14)]
+    ys = [8 * Delta(q) for q in qs]
+    # exact interpolation of a*q^2 + b*q + c through three points
+    (q0, q1, q2), (y0, y1, y2) = qs, ys
+    a = ((y2 - y1) / (q2 - q1) - (y1 - y0) / (q1 - q0)) / (q2 - q0)
+    b = (y1 - y0) / (q1 - q0) - a * (q1 + q0)
+    c = y0 - a * q0 ** 2 - b * q0
+    assert 8 * Delta(Fraction(20)) == a * 400 + b * 20 + c
+    disc = b * b - 4 * a * c
+    assert a > 0 and disc == Fraction(golden_lines("closed_forms.txt")[-2][1])
+
+
+def _D_vectorized(x):
+    """D(x) = E(x)/x^3 evaluated in binary64 from the implemented pieces."""
+    E = np.zeros_like(x)
+    for a, b, r in pieces():
+        a, b, r = float(a), float(b), float(r)
+        lo = np.minimum(np.maximum(x, a), b)
+        E += ((lo - r) ** 3 - (a - r) ** 3) / 3.0 * (x > a)
+    return E / x ** 3
+
+
+def _law_nodes(law, n=400000):
+    """Midpoint-rule nodes and weights for log2(M) under `law` (deterministic)."""
+    if law == "uniform01":
+        u = (np.arange(n) + 0.5) / n
+        return u, np.full(n, 1.0 / n)
+    if law == "mixture":
+        u1, w1 = _law_nodes(("normal", 0.3, 0.2), n // 2)
+        u2, w2 = _law_nodes(("normal", 2.7, 0.5), n // 2)
+        return np.concatenate([u1, u2]), np.concatenate([w1, w2]) * 0.5
+    _, mu, sd = law
+    u = mu + sd * (-8 + 16 * (np.arange(n) + 0.5) / n)
+    w = np.exp(-0.5 * ((u - mu) / sd) ** 2)
+    return u, w / w.sum()
+
+
+@pytest.mark.parametrize("law", ["uniform01", ("normal", 0.0, 0.1), ("normal", 3.0, 2.0), "mixture"])
+def test_uos_objective_minimized_at_7_25(law):
+    """Theorem 1 / Fig. 2: J(q) = E[D(X_q)] over the implemented ceiling rule and
+    projection has its minimum at q = 7.25 on the paper's 6.00..8.00 sweep grid
+    (step 0.05, Sec. 5.5.1), whatever the law of log2 M."""
+    u, w = _law_nodes(law)
+    M = np.exp2(u)
+    qs = np.round(np.arange(6.0, 8.0001, 0.05), 2)
+    J = []
+    for q in qs:
+        e = oracle.scale_exponents(M, oracle.RULE_CEIL_Q, q).astype(np.float64)
+        J.append(float(np.sum(w * _D_vectorized(M / np.exp2(e)))))
+    assert qs[int(np.argmin(J))] == 7.25
+
+
+def test_ocp_overflow_region_probability():
+    """Eq. 15: under a log-uniform block maximum, Pr(x_max >= 7) = log2(8/7)
+    for the OCP rule (the page's printed 19.27 % rounds the exact 0.192645)."""
+    n = 2_000_000
+    u = (np.arange(n) + 0.5) / n * 7.0 - 3.0  # seven whole binades
+    M = np.exp2(u)
+    e = oracle.scale_exponents(M, oracle.RULE_OCP).astype(np.float64)
+    p = float(np.mean(M / np.exp2(e) >= 7.0))
+    assert abs(p - math.log2(8 / 7)) < 2e-6
+    assert round(math.log2(8 / 7) * 100, 2) == 19.26
+
+
+# --------------------------------------------------------------------------
+# element decode and Hadamard rotation  [P1 Sec. 4.3, Alg. 2 steps 3-4; P2]
+
+
+def test_decode_half_exhaustive():
+    bits = np.arange(0, 1 << 16, dtype=np.uint16)
+    ref16 = bits.view(np.float16).astype(np.float32)
+    ref_bf = (bits.astype(np.uint32) << 16).view(np.float32)
+    got16 = np.array([oracle.decode_half(int(b), oracle.FP16) for b in bits], np.float32)
+    gotbf = np.array([oracle.decode_half(int(b), oracle.BF16) for b in bits], np.float32)
+    for got, ref in ((got16, ref16), (gotbf, ref_bf)):
+        nan = np.isnan(ref)
+        assert (np.isnan(got) == nan).all()
+        assert (got[~nan].view(np.uint32) == ref[~nan].view(np.uint32)).all()
+
+
+@pytest.mark.parametrize("d", [32, 64, 128, 256])
+def test_rotation_is_scaled_sylvester_hadamard(d):
+    H = scipy.linalg.hadamard(d).astype(np.float64)  # Sylvester construction
+    r = np.float32(1.0 / math.sqrt(d))
+    R = np.stack([oracle.hadamard_rotate_f32(np.eye(d, dtype=np.float32)[i]) for i in range(d)])
+    # e_i maps exactly to row i of H times fl32(1/sqrt d)
+    assert (R == (H * np.float64(r)).astype(np.float32)).all()
+    # orthogonality up to the rounding of fl32(1/sqrt d)
+    G = R.astype(np.float64) @ R.T.astype(np.float64)
+    assert np.allclose(G, np.eye(d) * d * float(r) ** 2, rtol=0, atol=1e-13)
+    assert abs(d * float(r) ** 2 - 1) < 2 ** -22
+    if d == 128:
+        assert int(np.array(r).view(np.uint32)) == 0x3DB504F3
+    if d == 64:
+        assert int(np.array(r).view(np.uint32)) == 0x3E000000
+    # the all-ones row concentrates on channel 0: sqrt(d) e_0
+    ones = oracle.hadamard_rotate_f32(np.ones(d, np.float32))
+    assert ones[0] == np.float32(d) * r and not ones[1:].any()
+
+
+def test_rotation_error_bound_norms_and_dot_products():
+    """Against x H / sqrt(d) in binary64 (scipy): each of log2(d) add stages and
+    the final multiply contributes at most 2^-24 relative, so the error is
+    bounded by (log2 d + 1) 2^-24 ||x||_1 / sqrt(d) (plus the same for the
+    binary64 reference).  Norms and dot products are preserved [P2 glossary]."""
+    rng = np.random.default_rng(3)
+    for d in (64, 128):
+        H = scipy.linalg.hadamard(d) / math.sqrt(d)
+        for _ in range(200):
+            x = (rng.standard_normal(d) * np.exp(rng.standard_normal(d))).astype(np.float32)
+            y = oracle.hadamard_rotate_f32(x).astype(np.float64)
+            ref = x.astype(np.float64) @ H
+            bound = (math.log2(d) + 2) * 2 ** -24 * np.abs(x).astype(np.float64).sum() / math.sqrt(d)
+            assert np.abs(y - ref).max() <= bound
+            assert abs(np.linalg.norm(ref) - np.linalg.norm(x.astype(np.float64))) < 1e-12 * np.linalg.norm(x)
+        q = rng.standard_normal(d)
+        k = rng.standard_normal(d)
+        assert abs((q @ H) @ (k @ H) - q @ k) < 1e-12 * (np.linalg.norm(q) * np.linalg.norm(k))
+
+
+def test_outlier_is_spread_over_every_channel():
+    """P2 'Rotate Q and K': a single outlier of magnitude A becomes magnitude
+    A/sqrt(d) on every channel."""
+    for d in (64, 128):
+        x = np.zeros(d, np.float32)
+        x[37] = 1000.0
+        y = oracle.hadamard_rotate_f32(x)
+        assert np.allclose(np.abs(y), 1000.0 / math.sqrt(d), rtol=2 ** -22)
+
+
+# --------------------------------------------------------------------------
+# tensor quantizers: axes and the block structure  [P3 Quantizing attention]
+
+
+def test_token_blocks_only_see_their_own_tokens():
+    """V is blocked along tokens (32 per block, aligned to token 0): changing
+    token j changes the codes/scales of block floor(j/32) only [P3]."""
+    N, d = 200, 64
+    x = W.custom(1, 1, N, d, seed=5, tensors=("v",))["v"]
+    c0, s0 = oracle.quantize_token_blocks(x, oracle.BF16, 1, 1, N, d)
+    for j in (0, 31, 32, 100, 199):
+        y = x.copy()
+        y[0, 0, j, :] = W.to_bits(np.full(d, 300.0), W.BF16)
+        c1, s1 = oracle.quantize_token_blocks(y, oracle.BF16, 1, 1, N, d)
+        changed = sorted(set(np.nonzero((c0 != c1).any(axis=(1, 2)) | (s0 != s1).any(axis=1))[0]))
+        assert changed == [j // 32]
+
+
+def test_row_quantizer_wiring_and_tail_block():
+    """Wiring only: rows assemble decode -> rotate -> 32-blocks along d; a
+    partial last token block is padded with +0."""
+    B, H, N, d = 2, 3, 45, 64
+    x = W.custom(B, H, N, d, dtype=W.FP16, seed=9, tensors=("q",))["q"]
+    codes, scales = oracle.quantize_rows(x, oracle.FP16, B, H, N, d, rotate=True)
+    g = (1 * H + 2) * N + 17
+    row = np.array([oracle.decode_half(int(b), oracle.FP16) for b in x[1, 2, 17]], np.float32)
+    row = oracle.hadamard_rotate_f32(row)
+    for k in range(d // 32):
+        sb, cc, _ = oracle.quantize_block(row[32 * k:32 * k + 32].astype(np.float64))
+        assert sb == scales[g, k] and (cc == codes[g, 32 * k:32 * k + 32]).all()
+    c, s = oracle.quantize_token_blocks(x, oracle.FP16, B, H, N, d)
+    NB = (N + 31) // 32
+    last = (0 * H + 0) * NB + NB - 1
+    # tokens 45..63 of the last block are padding: codes +0 (no sign bit)
+    assert (c[last][:, N - 32 * (NB - 1):] == 0).all()
+
+
+# --------------------------------------------------------------------------
+# attention forward  [P1 Alg. 2; Eqs. 1-8, 42, 44-52; App. H-J; P3]
+
+
+def dequant_rows(codes, scales):
+    grid = np.array([oracle.e2m1_magnitude(c) for c in range(8)])
+    v = grid[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    return v * np.exp2(np.repeat(scales.astype(np.float64) - 127, 32, axis=-1))
+
+
+def quantized_head(x_q, x_k, x_v, dtype, N, d, rotate=True, rule=oracle.RULE_UOS):
+    """q^, k^, v^ of a single head [N, d] in binary64 via the oracle's quantizers."""
+    cq, sq = oracle.quantize_rows(x_q, dtype, 1, 1, N, d, rotate=rotate, rule=rule)
+    ck, sk = oracle.quantize_rows(x_k, dtype, 1, 1, N, d, rotate=rotate, rule=rule)
+    cv, sv = oracle.quantize_token_blocks(x_v, dtype, 1, 1, N, d, rule=rule)
+    qh, kh = dequant_rows(cq, sq), dequant_rows(ck, sk)
+    grid = np.array([oracle.e2m1_magnitude(c) for c in range(8)])
+    vv = grid[cv & 7] * np.where(cv & 8, -1.0, 1.0) * np.exp2(sv.astype(np.float64) - 127)[..., None]
+    vh = vv.transpose(0, 2, 1).reshape(-1, d)[:N]
+    return qh, kh, vh
+
+
+def exact_attention(q, k, v, causal):
+    s = q @ k.T / math.sqrt(q.shape[1])
+    if causal:
+        s = np.where(np.tril(np.ones_like(s, dtype=bool)), s, -np.inf)
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    return (p / p.sum(axis=1, keepdims=True)) @ v
+
+
+@pytest.mark.parametrize("N", [1, 7, 100, 300])
+@pytest.mark.parametrize("causal", [False, True])
+def test_online_softmax_recurrence_equals_softmax_attention(N, causal):
+    """With quantization off, the tiled recurrence of Eqs. 2-8 equals the plain
+    softmax attention of Eq. 1 for every tile width [Sec. 2]."""
+    d = 64
+    x = W.custom(1, 2, N, d, seed=N, scale=2.0)
+    ref = [exact_attention(*(W.from_bits(x[t][0, h], W.BF16).astype(np.float64) for t in "qkv"), causal)
+           for h in range(2)]
+    for Bc in (32, 64, 128, 256):
+        r = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 2, N, d, causal=causal,
+                             rotate=False, quant=False, kv_tile=Bc)
+        for h in range(2):
+            assert np.allclose(r["out"][0, h], ref[h], rtol=1e-12, atol=1e-12)
+        assert np.allclose(r["rowsum"], 1.0, atol=1e-12)
+
+
+def test_pnq_rows_sum_to_one_and_l_at_least_one():
+    """Prop. 1 (Eq. 51) via the effective full-row form of Lemma 2 (Eqs. 99-105),
+    and App. J (Eq. 118): l >= 1 for every row."""
+    for w in (W.WORKLOADS[1],):
+        q, k, v = (W.generate(w, t) for t in "qkv")
+        r = oracle.attention(q, k, v, w.dtype, w.B, w.H, w.N, w.d)
+        assert np.abs(r["rowsum"] - 1.0).max() < 1e-12
+        assert (r["l"] >= 1.0).all()
+    x = W.custom(2, 2, 333, 64, seed=4, scale=3.0)
+    for causal in (False, True):
+        r = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 2, 2, 333, 64, causal=causal)
+        assert np.abs(r["rowsum"] - 1.0).max() < 1e-12
+        assert (r["l"] >= 1.0).all()
+
+
+def test_direct_placement_normalizer_and_row_sums():
+    """Direct placement (Eq. 42): l telescopes to the unquantized softmax
+    normalizer sum_j exp(s_j - m) (Eq. 108, computed here from scratch with
+    numpy), and the induced row sums (Eq. 110) are not 1 in general (Eq. 18)."""
+    N, d = 300, 128
+    x = W.custom(1, 1, N, d, seed=21, scale=1.5)
+    r = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, p_mode=oracle.P_DIRECT)
+    qh, kh, _ = quantized_head(x["q"], x["k"], x["v"], W.BF16, N, d)
+    s = qh @ kh.T / math.sqrt(d)
+    m = s.max(axis=1)
+    assert np.allclose(r["m"][0, 0], m, rtol=1e-14, atol=0)
+    assert np.allclose(r["l"][0, 0], np.exp(s - m[:, None]).sum(axis=1), rtol=1e-12)
+    rs = r["rowsum"][0, 0]
+    assert np.abs(rs - 1).max() > 1e-3
+    p = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, p_mode=oracle.P_PNQ)
+    assert np.abs(p["rowsum"] - 1).max() < 1e-12
+
+
+def test_closed_form_outputs():
+    """Derived from Alg. 2 and App. J:
+    (i) a single visible key gives O = v^_0 exactly;
+    (ii) Q = 0 makes every score equal, every P~ = 1 = P^, so O = mean_j v^_j;
+    (iii) V constant per channel gives, under PNQ, O = Q*(c) for any Q and K;
+          the direct placement gives rowsum * Q*(c) instead."""
+    d = 128
+    x = W.custom(1, 1, 1, d, seed=2)
+    r = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, 1, d)
+    _, _, vh = quantized_head(x["q"], x["k"], x["v"], W.BF16, 1, d)
+    assert (r["out"][0, 0, 0] == vh[0]).all()
+    N = 200
+    x = W.custom(1, 1, N, d, seed=3)
+    rc = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, causal=True, rows=[0])
+    _, _, vh = quantized_head(x["q"], x["k"], x["v"], W.BF16, N, d)
+    assert (rc["out"][0, 0, 0] == vh[0]).all()
+    zq = np.zeros_like(x["q"])
+    r0 = oracle.attention(zq, x["k"], x["v"], W.BF16, 1, 1, N, d)
+    assert np.allclose(r0["out"][0, 0], vh.mean(axis=0)[None, :], rtol=1e-13, atol=1e-13)
+    c = np.linspace(-5, 5, d)
+    cv = np.broadcast_to(W.to_bits(c, W.BF16), (1, 1, N, d)).copy()
+    xs = W.custom(1, 1, N, d, seed=8, scale=3.0)
+    rp = oracle.attention(xs["q"], xs["k"], cv, W.BF16, 1, 1, N, d)
+    _, _, vc = quantized_head(xs["q"], xs["k"], cv, W.BF16, N, d)
+    assert (vc == vc[0]).all()
+    assert np.allclose(rp["out"][0, 0], vc[0][None, :], rtol=1e-13, atol=1e-13)
+    rd = oracle.attention(xs["q"], xs["k"], cv, W.BF16, 1, 1, N, d, p_mode=oracle.P_DIRECT)
+    assert np.allclose(rd["out"][0, 0], rd["rowsum"][0, 0][:, None] * vc[0][None, :], rtol=1e-12,
+                       atol=1e-12)
+
+
+def test_causal_leakage_block_analysis():
+    """P3: with V blocked along tokens, perturbing V at j leaves rows i below
+    its block bit-identical, changes rows inside the block with i < j (the
+    leak), and perturbing K or Q at j leaves every row i < j bit-identical."""
+    N, d = 160, 128
+    x = W.custom(1, 1, N, d, seed=13)
+    base = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, causal=True)["out"][0, 0]
+    for j in (45, 100):
+        y = x["v"].copy()
+        y[0, 0, j] = W.to_bits(W.from_bits(y[0, 0, j], W.BF16).astype(np.float64) * 256.0, W.BF16)
+        o = oracle.attention(x["q"], x["k"], y, W.BF16, 1, 1, N, d, causal=True)["out"][0, 0]
+        blk0 = 32 * (j // 32)
+        assert (o[:blk0] == base[:blk0]).all()
+        assert (o[blk0:j] != base[blk0:j]).any(axis=1).all()
+        for t in ("k", "q"):
+            z = {kk: vv.copy() for kk, vv in x.items()}
+            z[t][0, 0, j] = W.to_bits(W.from_bits(z[t][0, 0, j], W.BF16).astype(np.float64) * -7.0, W.BF16)
+            o = oracle.attention(z["q"], z["k"], z["v"], W.BF16, 1, 1, N, d, causal=True)["out"][0, 0]
+            assert (o[:j] == base[:j]).all()
+
+
+def test_result_depends_on_tile_width_but_stays_normalized():
+    N, d = 256, 64
+    x = W.custom(1, 1, N, d, seed=17, scale=2.5)
+    outs = []
+    for Bc in (32, 64, 128):
+        r = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, kv_tile=Bc)
+        assert np.abs(r["rowsum"] - 1).max() < 1e-12
+        outs.append(r["out"])
+    assert np.abs(outs[0] - outs[1]).max() > 0 and np.abs(outs[1] - outs[2]).max() > 0
+
+
+def brute_force_pnq(qh, kh, vh, Bc, causal, rule=oracle.RULE_UOS, direct=False):
+    """Independent small re-statement of Alg. 2: materialize S, walk the tiles,
+    quantize each aligned 32-key block of exp(S - m_new) with the (separately
+    pinned) block quantizer."""
+    N, d = qh.shape
+    S = qh @ kh.T / math.sqrt(d)
+    out = np.zeros((N, d))
+    for i in range(N):
+        m, l, o = -np.inf, 0.0, np.zeros(d)
+        for j0 in range(0, N, Bc):
+            vis = [j for j in range(j0, min(j0 + Bc, N)) if (not causal or j <= i)]
+            if not vis:
+                continue
+            mn = max(m, max(S[i, j] for j in vis))
+            a = 0.0 if m == -np.inf else math.exp(m - mn)
+            pt = np.zeros(Bc)
+            for j in vis:
+                pt[j - j0] = math.exp(S[i, j] - mn)
+            ph = np.zeros(Bc)
+            for b0 in range(0, Bc, 32):
+                sb, codes, _ = oracle.quantize_block(pt[b0:b0 + 32], rule)
+                ph[b0:b0 + 32] = [oracle.e2m1_value(c) * 2.0 ** (sb - 127) for c in codes]
+            l = a * l + (pt.sum() if direct else ph.sum())
+            o = a * o + sum(ph[j - j0] * vh[j] for j in vis)
+            m = mn
+        out[i] = o / l
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,Bc", [(1, 32), (37, 32), (70, 64), (64, 128)])
+def test_brute_force_tiny(N, Bc, causal):
+    d = 32
+    x = W.custom(1, 1, N, d, seed=N + Bc, scale=2.0)
+    qh, kh, vh = quantized_head(x["q"], x["k"], x["v"], W.BF16, N, d)
+    for direct in (False, True):
+        ref = brute_force_pnq(qh, kh, vh, Bc, causal, direct=direct)
+        r = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, causal=causal, kv_tile=Bc,
+                             p_mode=oracle.P_DIRECT if direct else oracle.P_PNQ)
+        assert np.allclose(r["out"][0, 0], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_postnorm_mode_definition():
+    """Materialized-P diagnostic (Sec. 5.5.2): O = Q(P) V^ with P the exact
+    softmax and no renormalization; with V constant per channel O equals
+    (sum_j Q(P)_ij) * Q*(c), and the row sums differ from 1."""
+    N, d = 250, 64
+    xs = W.custom(1, 1, N, d, seed=31, scale=2.0)
+    c = np.linspace(-3, 3, d)
+    cv = np.broadcast_to(W.to_bits(c, W.BF16), (1, 1, N, d)).copy()
+    r = oracle.attention(xs["q"], xs["k"], cv, W.BF16, 1, 1, N, d, p_mode=oracle.P_POSTNORM)
+    _, _, vc = quantized_head(xs["q"], xs["k"], cv, W.BF16, N, d)
+    assert np.allclose(r["out"][0, 0], r["rowsum"][0, 0][:, None] * vc[0][None, :], rtol=1e-12, atol=1e-13)
+    assert np.abs(r["rowsum"] - 1).max() > 1e-3
+    qh, kh, _ = quantized_head(xs["q"], xs["k"], cv, W.BF16, N, d)
+    s = qh @ kh.T / math.sqrt(d)
+    assert np.allclose(r["l"][0, 0], np.exp(s - s.max(axis=1, keepdims=True)).sum(axis=1), rtol=1e-12)
+
+
+def test_decision_allowance_is_nonnegative_and_off_by_default():
+    w = W.WORKLOADS[1]
+    q, k, v = (W.generate(w, t) for t in "qkv")
+    r0 = oracle.attention(q, k, v, w.dtype, w.B, w.H, w.N, w.d)
+    assert (r0["amb"] == 0).all()
+    r1 = oracle.attention(q, k, v, w.dtype, w.B, w.H, w.N, w.d, amb_delta=1e-3)
+    assert (r1["amb"] >= 0).all() and r1["amb"].max() > 0
+    assert (r1["out"] == r0["out"]).all()
