@@ -1,0 +1,198 @@
+/*
+ * mxattn.h -- C ABI of libmxattn: MXAttention's MXFP4 attention forward for
+ * AMD Instinct MI355X (CDNA4, gfx950).
+ *
+ * The method (MXAttention, "Data-Free Optimal Scaling and Pre-Normalization
+ * Quantization for MXFP4 Attention"):
+ *   1. a fixed Hadamard rotation of Q and K (Sec. 4.3, Alg. 2 steps 3-4);
+ *   2. MXFP4 quantization of Q, K and V -- 32-element blocks of E2M1 values
+ *      sharing one E8M0 scale chosen by Universal Optimal Scaling,
+ *      e = ceil(log2(M / 7.25)) (Sec. 4.1, Alg. 1; Alg. 2 steps 5-7);
+ *   3. block-scaled FP4 matrix products QK^T and PV inside a tiled online
+ *      softmax (Sec. 2, Eqs. 2-8; Alg. 2 steps 8-21);
+ *   4. Pre-Normalization Quantization: the unnormalized exponential tile
+ *      exp(S - m) is quantized once, and that same quantized tile updates both
+ *      the row sum l and the output accumulator (Sec. 4.2, Eqs. 44-48).
+ *
+ * Conventions shared by every call
+ *   - Memory: the caller allocates every buffer (device memory unless noted)
+ *     and keeps ownership; the library allocates nothing and keeps no state
+ *     between calls.  Calls are thread-safe.
+ *   - Streams: work is enqueued on `stream` (0 = the null stream) and returns
+ *     without synchronizing; results are valid once the stream has reached
+ *     that point.
+ *   - Errors: every argument is validated before anything is enqueued; on an
+ *     error nothing is written and nothing is launched.  A launch failure
+ *     after validation returns MXATTN_ERR_HIP.
+ *   - Inputs must be finite.  Outputs for non-finite inputs are unspecified.
+ *   - Alignment: every device pointer must be 16-byte aligned.
+ *
+ * Layouts
+ *   Input tensors Q, K, V: 16-bit elements (bfloat16 or IEEE half), logical
+ *   shape [B, H, N, d].  `strides` gives the element strides of the B, H and N
+ *   dimensions (NULL = contiguous); the d dimension is contiguous.  Every
+ *   stride must be a multiple of 8 elements (16-byte aligned rows).
+ *
+ *   Let Np = N rounded up to a multiple of MXATTN_TOKEN_ALIGN (128).
+ *
+ *   MXFP4, head-dimension axis (Q^, K^):
+ *     codes  uint8 [B, H, Np, d/2]: byte k of a row holds element 2k in
+ *            bits 0-3 and element 2k+1 in bits 4-7; a 4-bit code is the
+ *            E2M1 value with the sign in bit 3 (magnitudes 0, .5, 1, 1.5, 2,
+ *            3, 4, 6 are codes 0..7);
+ *     scales uint8 [B, H, Np, d/32]: E8M0 byte, value 2^(byte - 127), of
+ *            elements 32j .. 32j+31 of the row.
+ *     Rows n >= N are written as zeros (codes 0, scale byte 127).
+ *   MXFP4, token axis (V^):
+ *     codes  uint8 [B, H, Np/32, d, 16]: for token block kb and channel c,
+ *            byte t holds token 32kb+2t in bits 0-3 and 32kb+2t+1 in 4-7;
+ *     scales uint8 [B, H, Np/32, d]: scale of tokens 32kb .. 32kb+31 of
+ *            channel c.
+ *     Tokens n >= N count as +0 (code 0); blocks with no token below N get
+ *     scale byte 127.
+ *
+ * Numerics of the quantizers (bit-exact contract)
+ *   - Rotation (Q, K): x <- x H_d / sqrt(d) with H_d the Sylvester Hadamard
+ *     matrix in natural order, computed in binary32 as butterflies of stride
+ *     1, 2, 4, ..., d/2 (each output one correctly rounded add/subtract),
+ *     then one multiply by fl32(1/sqrt(d)).
+ *   - Block scale: M = max |x_i|; an all-zero block gets 2^0.  Otherwise UOS
+ *     e = ceil(log2(M / 7.25)) or OCP e = floor(log2 M) - 2, clamped to
+ *     [-127, 127].
+ *   - Elements: x_i / 2^e rounded to the nearest E2M1 value, ties to the even
+ *     code, magnitudes above 6 saturating at 6; a value that rounds to zero
+ *     keeps its sign bit.
+ */
+#ifndef MXATTN_H
+#define MXATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXATTN_OK = 0,
+  MXATTN_ERR_NULL = 1,      /* a required pointer is NULL                          */
+  MXATTN_ERR_SHAPE = 2,     /* B, H or N < 1, d not 64 or 128, or sizes overflow    */
+  MXATTN_ERR_DTYPE = 3,     /* unknown dtype                                        */
+  MXATTN_ERR_ALIGN = 4,     /* a device pointer is not 16-byte aligned              */
+  MXATTN_ERR_STRIDE = 5,    /* a stride is negative or not a multiple of 8 elements */
+  MXATTN_ERR_MISMATCH = 6,  /* MXFP4 tensor descriptors disagree                    */
+  MXATTN_ERR_WORKSPACE = 7, /* workspace missing or smaller than required           */
+  MXATTN_ERR_ENUM = 8,      /* unknown axis, rule or P placement                    */
+  MXATTN_ERR_HIP = 9        /* a HIP runtime call or kernel launch failed           */
+} mxattn_status;
+
+typedef enum { MXATTN_BF16 = 0, MXATTN_FP16 = 1 } mxattn_dtype;
+typedef enum { MXATTN_AXIS_HEAD_DIM = 0, MXATTN_AXIS_TOKEN = 1 } mxattn_axis;
+/* Shared-scale rule: UOS (Sec. 4.1, Eq. 19 with q* = 7.25) or the OCP
+ * floor rule used by the vanilla baseline (Sec. 2, Eq. 11; App. G Eq. 97). */
+typedef enum { MXATTN_SCALE_UOS = 0, MXATTN_SCALE_OCP = 1 } mxattn_scale_rule;
+/* Placement of the softmax-path quantizer (Sec. 4.2; Sec. 5.5.2):
+ *   PNQ      l and O both updated from Q(P~)            (Eqs. 44-48)
+ *   DIRECT   l from P~, O from Q(P~)                     (Eq. 42 / Eqs. 16-17)
+ *   POSTNORM P = softmax(S) computed exactly first, then O = Q(P) V^ with no
+ *            renormalization (the materialized-P diagnostic of Sec. 5.5.2). */
+typedef enum { MXATTN_P_PNQ = 0, MXATTN_P_DIRECT = 1, MXATTN_P_POSTNORM = 2 } mxattn_p_mode;
+
+#define MXATTN_TOKEN_ALIGN 128
+
+typedef struct {
+  int32_t B, H, N, d;
+} mxattn_shape;
+
+/* Descriptor of a caller-owned MXFP4 tensor in one of the layouts above. */
+typedef struct {
+  uint8_t* codes;
+  uint8_t* scales;
+  mxattn_shape shape;
+  int32_t axis;    /* mxattn_axis       */
+  int32_t rule;    /* mxattn_scale_rule */
+  int32_t rotated; /* 1 if Hadamard-rotated before quantization */
+} mxattn_mx_tensor;
+
+/* Bytes of the codes / scales buffers of an MXFP4 tensor of `shape` blocked
+ * along `axis` (Np-padded layouts above).  0 for an invalid shape or axis. */
+size_t mxattn_mx_codes_bytes(mxattn_shape shape, int32_t axis);
+size_t mxattn_mx_scales_bytes(mxattn_shape shape, int32_t axis);
+
+/* Width B_c of the key/value tiles of the online-softmax loop of
+ * mxattn_forward (Alg. 2 step 10).  PNQ quantizes each exponential tile
+ * against the running maximum reached after that tile, so the result depends
+ * on B_c: it is part of the definition of the output.  Tiles are visited in
+ * ascending key order; the exponentials are quantized in 32-key blocks
+ * aligned to key 0.  Returns 128 for d in {64, 128}, 0 otherwise. */
+int32_t mxattn_forward_kv_tile(int32_t d, int32_t causal);
+
+/* Rotate (optionally) and quantize one tensor to MXFP4.
+ *   x        device pointer to the [B, H, N, d] 16-bit input
+ *   dtype    mxattn_dtype
+ *   strides  host array of 3 element strides (B, H, N) or NULL (contiguous)
+ *   axis     MXATTN_AXIS_HEAD_DIM (Q, K; Alg. 2 steps 5-6, blocks along d)
+ *            or MXATTN_AXIS_TOKEN (V; Alg. 2 step 7, blocks along tokens --
+ *            the block axis of the PV product's contraction, as the MatX
+ *            "leaky quantization" page describes)
+ *   rotate   1: apply the Hadamard rotation first (Alg. 2 steps 3-4); only
+ *            allowed with MXATTN_AXIS_HEAD_DIM
+ *   rule     mxattn_scale_rule
+ *   out      host descriptor: the caller sets out->codes and out->scales to
+ *            buffers of mxattn_mx_codes_bytes / mxattn_mx_scales_bytes; the
+ *            call fills shape, axis, rule and rotated.
+ * The padded rows/blocks are written too (see Layouts). */
+mxattn_status mxattn_rotate_quantize(const void* x, int32_t dtype, mxattn_shape shape,
+                                     const int64_t* strides, int32_t axis, int32_t rotate,
+                                     int32_t rule, mxattn_mx_tensor* out, hipStream_t stream);
+
+/* Fused MXFP4 attention forward with PNQ (Alg. 2 steps 8-22).
+ *   q, k     head-dimension MXFP4 tensors of one shape, both rotated or both
+ *            not (Q K^T is unchanged by the rotation only if both are)
+ *   v        token-axis MXFP4 tensor of the same shape
+ *   causal   1: key j is visible to query i iff j <= i
+ *   out      device float [B, H, N, d], contiguous: O = diag(l)^-1 O~ (Eq. 8)
+ *   row_stats device float [B, H, N, 2] or NULL: (m, l) per row, with m the
+ *            final running maximum of S = Q^ K^T / sqrt(d) and l the final
+ *            PNQ row sum (l >= 1, App. J)
+ * S, l and O~ accumulate in binary32.  The exponential tile is quantized
+ * with the UOS rule whatever the rule of the inputs. */
+mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* k,
+                             const mxattn_mx_tensor* v, int32_t causal, float* out,
+                             float* row_stats, hipStream_t stream);
+
+/* Workspace needed by mxattn_quantize_reference_modes for `shape`/`p_mode`
+ * (the three MXFP4 tensors, plus per-row statistics for POSTNORM).
+ * 0 for an invalid shape or mode. */
+size_t mxattn_reference_modes_workspace_bytes(mxattn_shape shape, int32_t p_mode);
+
+/* The compared configurations of the ablation (Sec. 5.2, Sec. 5.4) and the
+ * materialized-P diagnostic (Sec. 5.5.2), end to end from 16-bit Q, K, V:
+ * quantize all three with `rule` (rotating Q and K if `rotate`), then run the
+ * forward with the softmax-path placement `p_mode`, quantizing the
+ * exponential (or probability) tiles with the same `rule`.
+ *   rule=OCP, p_mode=DIRECT, rotate=0 is the vanilla OCP MXFP4 baseline;
+ *   rule=UOS, p_mode=PNQ, rotate=1 equals rotate_quantize x3 + forward.
+ *   out       device float [B, H, N, d], contiguous
+ *   row_sums  device float [B, H, N] or NULL: the induced sum of the
+ *             normalized attention weights of each row -- PNQ: 1 up to
+ *             rounding (Prop. 1); DIRECT: (sum beta P^ 1) / l (App. I,
+ *             Eq. 110); POSTNORM: sum_j Q(P)_ij
+ *   workspace device buffer of at least
+ *             mxattn_reference_modes_workspace_bytes(shape, p_mode) bytes */
+mxattn_status mxattn_quantize_reference_modes(const void* q, const void* k, const void* v,
+                                              int32_t dtype, mxattn_shape shape,
+                                              const int64_t* strides, int32_t rule,
+                                              int32_t p_mode, int32_t rotate, int32_t causal,
+                                              float* out, float* row_sums, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* mxattn_status_string(mxattn_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXATTN_H */

@@ -1,0 +1,232 @@
+// C ABI of libmxattn (include/mxattn.h): argument validation, buffer sizes
+// and dispatch to the HIP kernels.  Nothing here allocates device memory or
+// keeps state between calls.
+#include "mxattn.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+using namespace mxattn_internal;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 44;  // keeps every index and grid in range
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+mxattn_status check_shape(const mxattn_shape& s) {
+  if (s.B < 1 || s.H < 1 || s.N < 1) return MXATTN_ERR_SHAPE;
+  if (s.d != 64 && s.d != 128) return MXATTN_ERR_SHAPE;
+  const int64_t Np = padded_tokens(s.N);
+  if ((int64_t)s.B * s.H > ((int64_t)1 << 30) / (Np / kTokenAlign)) return MXATTN_ERR_SHAPE;
+  if ((int64_t)s.B * s.H * Np * s.d > kMaxElems) return MXATTN_ERR_SHAPE;
+  return MXATTN_OK;
+}
+
+bool same_shape(const mxattn_shape& a, const mxattn_shape& b) {
+  return a.B == b.B && a.H == b.H && a.N == b.N && a.d == b.d;
+}
+
+// element strides of the B, H, N dimensions (d is contiguous)
+mxattn_status resolve_strides(const mxattn_shape& s, const int64_t* strides, int64_t out[3]) {
+  if (!strides) {
+    out[2] = s.d;
+    out[1] = (int64_t)s.N * s.d;
+    out[0] = (int64_t)s.H * s.N * s.d;
+    return MXATTN_OK;
+  }
+  for (int i = 0; i < 3; ++i) {
+    if (strides[i] < 0 || (strides[i] & 7) != 0) return MXATTN_ERR_STRIDE;
+    out[i] = strides[i];
+  }
+  // rows of one (b, h) must not overlap inside a row
+  if (s.N > 1 && out[2] < s.d) return MXATTN_ERR_STRIDE;
+  return MXATTN_OK;
+}
+
+size_t codes_bytes(const mxattn_shape& s, int axis) {
+  const int64_t Np = padded_tokens(s.N);
+  (void)axis;  // both axes: d/2 bytes per padded token
+  return (size_t)((int64_t)s.B * s.H * Np * (s.d / 2));
+}
+
+size_t scales_bytes(const mxattn_shape& s, int axis) {
+  const int64_t Np = padded_tokens(s.N);
+  (void)axis;  // both axes: d/32 bytes per padded token
+  return (size_t)((int64_t)s.B * s.H * Np * (s.d / 32));
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+mxattn_status hip_status(hipError_t e) { return e == hipSuccess ? MXATTN_OK : MXATTN_ERR_HIP; }
+
+mxattn_status check_mx(const mxattn_mx_tensor* t, int axis) {
+  if (!t || !t->codes || !t->scales) return MXATTN_ERR_NULL;
+  if (t->axis != axis) return MXATTN_ERR_MISMATCH;
+  mxattn_status st = check_shape(t->shape);
+  if (st != MXATTN_OK) return st;
+  if (!aligned16(t->codes) || !aligned16(t->scales)) return MXATTN_ERR_ALIGN;
+  return MXATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mxattn_mx_codes_bytes(mxattn_shape shape, int32_t axis) {
+  if (check_shape(shape) != MXATTN_OK || (axis != MXATTN_AXIS_HEAD_DIM && axis != MXATTN_AXIS_TOKEN)) return 0;
+  return codes_bytes(shape, axis);
+}
+
+size_t mxattn_mx_scales_bytes(mxattn_shape shape, int32_t axis) {
+  if (check_shape(shape) != MXATTN_OK || (axis != MXATTN_AXIS_HEAD_DIM && axis != MXATTN_AXIS_TOKEN)) return 0;
+  return scales_bytes(shape, axis);
+}
+
+int32_t mxattn_forward_kv_tile(int32_t d, int32_t causal) {
+  (void)causal;
+  return (d == 64 || d == 128) ? kKvTile : 0;
+}
+
+mxattn_status mxattn_rotate_quantize(const void* x, int32_t dtype, mxattn_shape shape,
+                                     const int64_t* strides, int32_t axis, int32_t rotate,
+                                     int32_t rule, mxattn_mx_tensor* out, hipStream_t stream) {
+  if (!x || !out || !out->codes || !out->scales) return MXATTN_ERR_NULL;
+  if (dtype != MXATTN_BF16 && dtype != MXATTN_FP16) return MXATTN_ERR_DTYPE;
+  if (axis != MXATTN_AXIS_HEAD_DIM && axis != MXATTN_AXIS_TOKEN) return MXATTN_ERR_ENUM;
+  if (rule != MXATTN_SCALE_UOS && rule != MXATTN_SCALE_OCP) return MXATTN_ERR_ENUM;
+  if (rotate != 0 && rotate != 1) return MXATTN_ERR_ENUM;
+  if (rotate && axis != MXATTN_AXIS_HEAD_DIM) return MXATTN_ERR_ENUM;
+  mxattn_status st = check_shape(shape);
+  if (st != MXATTN_OK) return st;
+  int64_t s[3];
+  st = resolve_strides(shape, strides, s);
+  if (st != MXATTN_OK) return st;
+  if (!aligned16(x) || !aligned16(out->codes) || !aligned16(out->scales)) return MXATTN_ERR_ALIGN;
+
+  QuantArgs a;
+  a.x = x;
+  a.dtype = dtype;
+  a.B = shape.B; a.H = shape.H; a.N = shape.N; a.d = shape.d;
+  a.sB = s[0]; a.sH = s[1]; a.sN = s[2];
+  a.rotate = rotate;
+  a.rule = rule;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  out->shape = shape;
+  out->axis = axis;
+  out->rule = rule;
+  out->rotated = rotate;
+  return hip_status(axis == MXATTN_AXIS_HEAD_DIM ? launch_quantize_headdim(a, stream)
+                                                 : launch_quantize_tokens(a, stream));
+}
+
+mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* k,
+                             const mxattn_mx_tensor* v, int32_t causal, float* out,
+                             float* row_stats, hipStream_t stream) {
+  if (!out) return MXATTN_ERR_NULL;
+  mxattn_status st = check_mx(q, MXATTN_AXIS_HEAD_DIM);
+  if (st != MXATTN_OK) return st;
+  st = check_mx(k, MXATTN_AXIS_HEAD_DIM);
+  if (st != MXATTN_OK) return st;
+  st = check_mx(v, MXATTN_AXIS_TOKEN);
+  if (st != MXATTN_OK) return st;
+  if (!same_shape(q->shape, k->shape) || !same_shape(q->shape, v->shape)) return MXATTN_ERR_MISMATCH;
+  if ((q->rotated != 0) != (k->rotated != 0)) return MXATTN_ERR_MISMATCH;
+  if (causal != 0 && causal != 1) return MXATTN_ERR_ENUM;
+  if (!aligned16(out) || (row_stats && !aligned16(row_stats))) return MXATTN_ERR_ALIGN;
+
+  AttnArgs a;
+  a.qc = q->codes; a.qs = q->scales;
+  a.kc = k->codes; a.ks = k->scales;
+  a.vc = v->codes; a.vs = v->scales;
+  a.B = q->shape.B; a.H = q->shape.H; a.N = q->shape.N; a.d = q->shape.d;
+  a.causal = causal;
+  a.mode = kModePnq;
+  a.rule = MXATTN_SCALE_UOS;
+  a.out = out;
+  a.row_stats = row_stats;
+  a.row_sums = nullptr;
+  a.stats_ws = nullptr;
+  return hip_status(launch_attention(a, stream));
+}
+
+size_t mxattn_reference_modes_workspace_bytes(mxattn_shape shape, int32_t p_mode) {
+  if (check_shape(shape) != MXATTN_OK) return 0;
+  if (p_mode != MXATTN_P_PNQ && p_mode != MXATTN_P_DIRECT && p_mode != MXATTN_P_POSTNORM) return 0;
+  size_t total = 3 * (round256(codes_bytes(shape, 0)) + round256(scales_bytes(shape, 0)));
+  if (p_mode == MXATTN_P_POSTNORM)
+    total += round256((size_t)shape.B * shape.H * padded_tokens(shape.N) * 2 * sizeof(float));
+  return total;
+}
+
+mxattn_status mxattn_quantize_reference_modes(const void* q, const void* k, const void* v,
+                                              int32_t dtype, mxattn_shape shape,
+                                              const int64_t* strides, int32_t rule,
+                                              int32_t p_mode, int32_t rotate, int32_t causal,
+                                              float* out, float* row_sums, void* workspace,
+                                              size_t workspace_bytes, hipStream_t stream) {
+  if (!q || !k || !v || !out) return MXATTN_ERR_NULL;
+  if (dtype != MXATTN_BF16 && dtype != MXATTN_FP16) return MXATTN_ERR_DTYPE;
+  if (rule != MXATTN_SCALE_UOS && rule != MXATTN_SCALE_OCP) return MXATTN_ERR_ENUM;
+  if (p_mode != MXATTN_P_PNQ && p_mode != MXATTN_P_DIRECT && p_mode != MXATTN_P_POSTNORM) return MXATTN_ERR_ENUM;
+  if ((rotate != 0 && rotate != 1) || (causal != 0 && causal != 1)) return MXATTN_ERR_ENUM;
+  mxattn_status st = check_shape(shape);
+  if (st != MXATTN_OK) return st;
+  int64_t s[3];
+  st = resolve_strides(shape, strides, s);
+  if (st != MXATTN_OK) return st;
+  const size_t need = mxattn_reference_modes_workspace_bytes(shape, p_mode);
+  if (!workspace || workspace_bytes < need) return MXATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(workspace) ||
+      (row_sums && !aligned16(row_sums)))
+    return MXATTN_ERR_ALIGN;
+
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  const size_t cb = round256(codes_bytes(shape, 0)), sb = round256(scales_bytes(shape, 0));
+  mxattn_mx_tensor tq = {w, w + cb, shape, 0, 0, 0};
+  mxattn_mx_tensor tk = {w + cb + sb, w + 2 * cb + sb, shape, 0, 0, 0};
+  mxattn_mx_tensor tv = {w + 2 * (cb + sb), w + 3 * cb + 2 * sb, shape, 0, 0, 0};
+  float* stats = reinterpret_cast<float*>(w + 3 * (cb + sb));
+
+  st = mxattn_rotate_quantize(q, dtype, shape, strides, MXATTN_AXIS_HEAD_DIM, rotate, rule, &tq, stream);
+  if (st != MXATTN_OK) return st;
+  st = mxattn_rotate_quantize(k, dtype, shape, strides, MXATTN_AXIS_HEAD_DIM, rotate, rule, &tk, stream);
+  if (st != MXATTN_OK) return st;
+  st = mxattn_rotate_quantize(v, dtype, shape, strides, MXATTN_AXIS_TOKEN, 0, rule, &tv, stream);
+  if (st != MXATTN_OK) return st;
+
+  AttnArgs a;
+  a.qc = tq.codes; a.qs = tq.scales;
+  a.kc = tk.codes; a.ks = tk.scales;
+  a.vc = tv.codes; a.vs = tv.scales;
+  a.B = shape.B; a.H = shape.H; a.N = shape.N; a.d = shape.d;
+  a.causal = causal;
+  a.mode = p_mode == MXATTN_P_PNQ ? kModePnq : (p_mode == MXATTN_P_DIRECT ? kModeDirect : kModePostnorm);
+  a.rule = rule;
+  a.out = out;
+  a.row_stats = nullptr;
+  a.row_sums = row_sums;
+  a.stats_ws = p_mode == MXATTN_P_POSTNORM ? stats : nullptr;
+  return hip_status(launch_attention(a, stream));
+}
+
+const char* mxattn_status_string(mxattn_status status) {
+  switch (status) {
+    case MXATTN_OK: return "ok";
+    case MXATTN_ERR_NULL: return "a required pointer is NULL";
+    case MXATTN_ERR_SHAPE: return "unsupported shape (B, H, N >= 1; d in {64, 128})";
+    case MXATTN_ERR_DTYPE: return "unknown input dtype";
+    case MXATTN_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case MXATTN_ERR_STRIDE: return "strides must be non-negative multiples of 8 elements";
+    case MXATTN_ERR_MISMATCH: return "MXFP4 tensor descriptors disagree";
+    case MXATTN_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXATTN_ERR_ENUM: return "unknown axis, rule, placement or flag value";
+    case MXATTN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

@@ -317,7 +317,7 @@ typedef struct {
   const int32_t* rows;
   int32_t n_rows;
   int32_t chunks_per_head, rows_per_chunk;
-  double *out, *m_out, *l_out, *rowsum, *amb;
+  double *out, *m_out, *l_out, *rowsum, *amb, *absmass;
 } attn_ctx;
 
 /* Dequantized (or plain) K and V of one head, and the query row, in binary64. */
@@ -450,6 +450,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
   double* qv = (double*)s; s += sizeof(double) * d;
   double* o = (double*)s;  s += sizeof(double) * d;
   double* ao = (double*)s; s += sizeof(double) * d;
+  double* am = (double*)s; s += sizeof(double) * d;  /* sum of |P^ V^| terms */
   double* sc = (double*)s; s += sizeof(double) * (size_t)N;   /* scores of the row  */
   double* pt = (double*)s; s += sizeof(double) * (size_t)(T * Bc); /* P~ (tile-padded) */
   double* ph = (double*)s; s += sizeof(double) * (size_t)(T * Bc); /* P^              */
@@ -479,8 +480,9 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
     }
     double* orow = c->out + (bh * c->n_rows + r) * d;
     double* arow = c->amb ? c->amb + (bh * c->n_rows + r) * d : NULL;
+    double* mrow = c->absmass ? c->absmass + (bh * c->n_rows + r) * d : NULL;
     const int64_t ridx = bh * c->n_rows + r;
-    for (int t = 0; t < d; ++t) { o[t] = 0.0; ao[t] = 0.0; }
+    for (int t = 0; t < d; ++t) { o[t] = 0.0; ao[t] = 0.0; am[t] = 0.0; }
 
     if (g->p_mode == ORACLE_P_POSTNORM && g->quant) {
       /* Materialized-P diagnostic [P1 Sec. 5.5.2]: exact softmax first, then
@@ -497,11 +499,13 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
         for (int t = 0; t < 32 && j0 + t < jvis; ++t) {
           sum_hat += hb[t];
           for (int ch = 0; ch < d; ++ch) o[ch] += hb[t] * V[(int64_t)(j0 + t) * d + ch];
+          for (int ch = 0; ch < d; ++ch) am[ch] += hb[t] * fabs(V[(int64_t)(j0 + t) * d + ch]);
           if (want_amb)
             for (int ch = 0; ch < d; ++ch) ao[ch] += db[t] * fabs(V[(int64_t)(j0 + t) * d + ch]);
         }
       }
       for (int ch = 0; ch < d; ++ch) orow[ch] = o[ch];
+      if (mrow) for (int ch = 0; ch < d; ++ch) mrow[ch] = am[ch];
       if (arow) for (int ch = 0; ch < d; ++ch) arow[ch] = want_amb ? ao[ch] : 0.0;
       if (c->m_out) c->m_out[ridx] = ms;
       if (c->l_out) c->l_out[ridx] = ls;
@@ -536,11 +540,14 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
       /* l update: Eq. 47 (PNQ) or Eq. 16 / Eq. 42 (direct) */
       l = alpha * l + ((g->p_mode == ORACLE_P_DIRECT && quantize_p) ? sum_til : sum_hat);
       /* O update: Eq. 48 / Eq. 17 */
-      for (int ch = 0; ch < d; ++ch) o[ch] *= alpha;
+      for (int ch = 0; ch < d; ++ch) { o[ch] *= alpha; am[ch] *= alpha; }
       for (int j = j0; j < j1; ++j) {
         const double w = Ph[j - j0];
         if (w != 0.0)
-          for (int ch = 0; ch < d; ++ch) o[ch] += w * V[(int64_t)j * d + ch];
+          for (int ch = 0; ch < d; ++ch) {
+            o[ch] += w * V[(int64_t)j * d + ch];
+            am[ch] += w * fabs(V[(int64_t)j * d + ch]);
+          }
       }
       if (want_amb) {
         double dl = 0.0;
@@ -561,6 +568,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
     /* O_i = o / l  [Eq. 8; Alg. 2 step 20]; POSTNORM without quantization
      * reduces to the same exact softmax attention. */
     for (int ch = 0; ch < d; ++ch) orow[ch] = o[ch] / l;
+    if (mrow) for (int ch = 0; ch < d; ++ch) mrow[ch] = am[ch] / l;
     if (arow) {
       for (int ch = 0; ch < d; ++ch) {
         if (!want_amb) arow[ch] = 0.0;
@@ -589,7 +597,7 @@ int oracle_attention(const oracle_attn_cfg* cfg,
                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const int64_t* strides, const int32_t* rows, int32_t n_rows,
                      double* out, double* m_out, double* l_out, double* rowsum,
-                     double* amb) {
+                     double* amb, double* absmass) {
   if (!cfg || !q || !k || !v || !out) return -1;
   if (!shape_ok(cfg->B, cfg->H, cfg->N, cfg->d)) return -1;
   if (cfg->kv_tile < 32 || cfg->kv_tile % 32 != 0) return -1;
@@ -607,6 +615,7 @@ int oracle_attention(const oracle_attn_cfg* cfg,
   c.rows = rows;
   c.n_rows = n_rows;
   c.out = out; c.m_out = m_out; c.l_out = l_out; c.rowsum = rowsum; c.amb = amb;
+  c.absmass = absmass;
   const int64_t heads = (int64_t)cfg->B * cfg->H;
   int nth = cfg->nthreads > 0 ? cfg->nthreads : 1;
   int cph = (int)((2 * (int64_t)nth + heads - 1) / heads);
@@ -615,7 +624,7 @@ int oracle_attention(const oracle_attn_cfg* cfg,
   c.chunks_per_head = cph;
   c.rows_per_chunk = (n_rows + cph - 1) / cph;
   const int N = cfg->N, d = cfg->d, T = (N + cfg->kv_tile - 1) / cfg->kv_tile;
-  size_t scratch = sizeof(double) * ((size_t)2 * N * d + 3 * (size_t)d + N + 3 * (size_t)T * cfg->kv_tile +
+  size_t scratch = sizeof(double) * ((size_t)2 * N * d + 4 * (size_t)d + N + 3 * (size_t)T * cfg->kv_tile +
                                      3 * (size_t)T + 32) +
                    sizeof(float) * d + 64;
   return run_pool(attn_item, &c, heads * cph, scratch, nth);

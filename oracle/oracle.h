@@ -137,12 +137,16 @@ typedef struct {
  *                               every P-quantizer decision lying within
  *                               relative margin amb_delta of its threshold
  *                               goes the other way; nullable
+ *   absmass  [B][H][n_rows][d]  the output computed with |V^| in place of V^
+ *                               (sum_j beta_j P^_j |v^_j| / l), the scale of
+ *                               rounding errors of any accumulation order;
+ *                               nullable
  * Returns 0, or -1 on a bad argument. */
 int oracle_attention(const oracle_attn_cfg* cfg,
                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const int64_t* strides, const int32_t* rows, int32_t n_rows,
                      double* out, double* m_out, double* l_out, double* rowsum,
-                     double* amb);
+                     double* amb, double* absmass);
 
 #ifdef __cplusplus
 }

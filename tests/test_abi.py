@@ -1,0 +1,135 @@
+"""CPU checks of the C-ABI library: it loads, exports every function the header
+declares, computes buffer sizes, and rejects bad arguments before touching
+the GPU (nothing here launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mxfp4_microscaled_bit_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxattn.h")
+
+FAKE = 0x100000  # 16-byte-aligned address never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxattn_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    L = mx.lib()
+    names = declared_functions()
+    assert set(names) == set(mx.EXPORTED)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_sizes_and_tile():
+    # Np = N rounded up to 128; head-dim codes d/2 and scales d/32 bytes per token
+    assert mx.mx_codes_bytes(1, 2, 256, 128, mx.AXIS_HEAD_DIM) == 2 * 256 * 64
+    assert mx.mx_scales_bytes(1, 2, 256, 128, mx.AXIS_HEAD_DIM) == 2 * 256 * 4
+    assert mx.mx_codes_bytes(1, 40, 32760, 128, mx.AXIS_TOKEN) == 40 * 32768 * 64
+    assert mx.mx_scales_bytes(16, 16, 4096, 64, mx.AXIS_TOKEN) == 256 * 4096 * 2
+    assert mx.mx_codes_bytes(1, 1, 1, 64) == 128 * 32
+    assert mx.mx_codes_bytes(1, 1, 1, 96) == 0
+    assert mx.mx_codes_bytes(1, 1, 0, 64) == 0
+    assert mx.mx_codes_bytes(1, 1, 5, 64, 7) == 0
+    assert mx.forward_kv_tile(128) == 128 and mx.forward_kv_tile(64, True) == 128
+    assert mx.forward_kv_tile(80) == 0
+    ws = mx.reference_modes_workspace_bytes(1, 2, 256, 128, mx.P_POSTNORM)
+    assert ws >= 3 * (2 * 256 * 64 + 2 * 256 * 4) + 2 * 256 * 2 * 4
+    assert mx.reference_modes_workspace_bytes(1, 2, 256, 128, 9) == 0
+
+
+def test_status_strings():
+    for s in range(10):
+        assert mx.status_string(s)
+    assert "unknown" in mx.status_string(42)
+
+
+def _desc(axis, B=1, H=1, N=64, d=64, codes=FAKE, scales=FAKE, rotated=1):
+    return mx.MXTensorDesc(codes, scales, mx.Shape(B, H, N, d), axis, 0, rotated)
+
+
+def _rq(x=FAKE, dtype=mx.BF16, shape=(1, 1, 64, 64), strides=None, axis=0, rotate=1, rule=0, out=None):
+    L = mx.lib()
+    if out is None:
+        out = mx.MXTensorDesc(FAKE, FAKE + 4096, mx.Shape(0, 0, 0, 0), 5, 5, 5)
+    st = None if strides is None else (ctypes.c_int64 * 3)(*strides)
+    return L.mxattn_rotate_quantize(x, dtype, mx.Shape(*shape), st, axis, rotate, rule, ctypes.byref(out),
+                                    None), out
+
+
+def test_rotate_quantize_rejects_bad_arguments_without_writing():
+    cases = [
+        (dict(x=None), 1),
+        (dict(out=mx.MXTensorDesc(None, FAKE, mx.Shape(0, 0, 0, 0), 5, 5, 5)), 1),
+        (dict(shape=(1, 1, 64, 96)), 2),
+        (dict(shape=(0, 1, 64, 64)), 2),
+        (dict(shape=(1, 1, 0, 64)), 2),
+        (dict(dtype=7), 3),
+        (dict(x=FAKE + 8), 4),
+        (dict(strides=(4096, 4096, 60)), 5),
+        (dict(strides=(4096, -64, 64)), 5),
+        (dict(strides=(4096, 4096, 32)), 5),
+        (dict(axis=3), 8),
+        (dict(rule=2), 8),
+        (dict(axis=1, rotate=1), 8),
+        (dict(rotate=2), 8),
+    ]
+    for kwargs, expect in cases:
+        status, out = _rq(**kwargs)
+        assert status == expect, (kwargs, status)
+        # on error the descriptor is not touched
+        if "out" not in kwargs:
+            assert (out.axis, out.rule, out.rotated, out.shape.N) == (5, 5, 5, 0)
+
+
+def test_forward_rejects_bad_arguments():
+    L = mx.lib()
+
+    def fwd(q=None, k=None, v=None, causal=0, out=FAKE, stats=None):
+        q = q or _desc(0)
+        k = k or _desc(0)
+        v = v or _desc(1)
+        return L.mxattn_forward(ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), causal, out, stats, None)
+
+    assert fwd(out=None) == 1
+    assert fwd(q=_desc(0, codes=None)) == 1
+    assert fwd(k=_desc(1)) == 6          # K must be head-dim blocked
+    assert fwd(v=_desc(0)) == 6          # V must be token blocked
+    assert fwd(k=_desc(0, N=65)) == 6    # shapes disagree
+    assert fwd(k=_desc(0, rotated=0)) == 6  # Q rotated, K not
+    assert fwd(v=_desc(1, d=96)) == 2
+    assert fwd(causal=2) == 8
+    assert fwd(out=FAKE + 4) == 4
+    assert fwd(stats=FAKE + 4) == 4
+    assert fwd(q=_desc(0, scales=FAKE + 1)) == 4
+
+
+def test_reference_modes_reject_bad_arguments():
+    L = mx.lib()
+    need = mx.reference_modes_workspace_bytes(1, 1, 64, 64, mx.P_DIRECT)
+
+    def ref(q=FAKE, rule=0, p_mode=1, rotate=0, causal=0, ws=FAKE, ws_bytes=None, out=FAKE, shape=(1, 1, 64, 64),
+            dtype=0, sums=None):
+        return L.mxattn_quantize_reference_modes(q, FAKE, FAKE, dtype, mx.Shape(*shape), None, rule, p_mode, rotate,
+                                                 causal, out, sums, ws, need if ws_bytes is None else ws_bytes, None)
+
+    assert ref(q=None) == 1
+    assert ref(out=None) == 1
+    assert ref(dtype=3) == 3
+    assert ref(rule=5) == 8
+    assert ref(p_mode=3) == 8
+    assert ref(rotate=3) == 8
+    assert ref(causal=-1) == 8
+    assert ref(shape=(1, 1, 64, 32)) == 2
+    assert ref(ws=None) == 7
+    assert ref(ws_bytes=need - 1) == 7
+    assert ref(q=FAKE + 2) == 4
+    assert ref(sums=FAKE + 12) == 4

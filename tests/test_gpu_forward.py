@@ -1,0 +1,234 @@
+"""GPU parity of the fused MXFP4 attention forward (and its reference modes)
+with the CPU oracle, plus oracle-free invariants of the method on the GPU."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_microscaled_bit_amd as mx
+import oracle
+import workloads as W
+from parity import DELTA, check_output, run_forward, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+KV_TILE = 128
+
+
+def _sample_rows(N, n_random, seed, causal=False):
+    rng = np.random.default_rng(seed)
+    rows = {0, 1, N - 1, N - 2, 127, 128, 129, N // 2}
+    rows.update(range(max(0, N - 130), N, 37))
+    rows.update(rng.integers(0, N, n_random).tolist())
+    return np.array(sorted(r for r in rows if 0 <= r < N), np.int32)
+
+
+def _oracle_heads(w, heads, rows, p_mode=oracle.P_PNQ, rule=oracle.RULE_UOS, rotate=True, bits=None):
+    """Oracle on the listed (b, h) heads only: they are independent, so the
+    oracle sees a [1, len(heads), N, d] problem."""
+    sel = {t: (bits[t][[b for b, _ in heads], [h for _, h in heads]][None] if bits else
+               W.generate(w, t, heads=heads)[None]) for t in "qkv"}
+    return oracle.attention(sel["q"], sel["k"], sel["v"], w.dtype, 1, len(heads), w.N, w.d, causal=w.causal,
+                            rotate=rotate, rule=rule, p_mode=p_mode, kv_tile=KV_TILE, rows=rows,
+                            amb_delta=DELTA)
+
+
+def _gpu_rows(out, heads, rows):
+    o = out.cpu().numpy() if isinstance(out, torch.Tensor) else out
+    return np.stack([o[b, h][rows] for b, h in heads])[None]
+
+
+WORKLOAD_SAMPLING = {
+    # cid: (heads to compare, random rows per head)
+    1: (None, None),
+    5: ([(0, 0), (3, 7), (9, 2), (15, 15)], 60),
+    4: ([(0, 0), (1, 17), (3, 31)], 60),
+    2: ([(0, 0), (0, 19), (0, 39)], 40),
+    3: ([(0, 0), (0, 23)], 16),
+}
+
+
+@pytest.mark.parametrize("cid", [1, 5, 4, 2, 3])
+def test_forward_matches_oracle(cid):
+    w = W.WORKLOADS[cid]
+    B, H, N, d = w.shape
+    say(f"forward parity: workload {cid} {w.describe()}")
+    bits = {t: W.generate(w, t) for t in "qkv"}
+    dev = {t: to_device(bits[t], w.dtype) for t in "qkv"}
+    out, stats = run_forward(dev["q"], dev["k"], dev["v"], w.causal)
+    heads, nrand = WORKLOAD_SAMPLING[cid]
+    if heads is None:
+        heads = [(b, h) for b in range(B) for h in range(H)]
+        rows = np.arange(N, dtype=np.int32)
+    else:
+        rows = _sample_rows(N, nrand, cid, w.causal)
+    ref = _oracle_heads(w, heads, rows, bits=bits)
+    gpu = _gpu_rows(out, heads, rows)
+    n_tiles = (N + KV_TILE - 1) // KV_TILE
+    check_output(gpu, ref, f"workload {cid} PNQ", n_tiles)
+    st = _gpu_rows(stats, heads, rows)
+    # App. J: l >= 1 for every row; l and m agree with the oracle
+    assert (st[..., 1] >= 1.0).all()
+    lrel = np.abs(st[..., 1] - ref["l"]) / ref["l"]
+    say(f"  l: max rel diff {lrel.max():.2e}; m: max abs diff {np.abs(st[..., 0] - ref['m']).max():.2e}")
+    assert ((lrel <= 1e-4) | (ref["amb"].max(axis=-1) > 0)).all()
+    assert np.allclose(st[..., 0], ref["m"], rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("p_mode,rule,rotate", [
+    (mx.P_PNQ, mx.SCALE_UOS, True),
+    (mx.P_PNQ, mx.SCALE_OCP, True),
+    (mx.P_DIRECT, mx.SCALE_OCP, False),   # vanilla OCP MXFP4 baseline (Sec. 5.2)
+    (mx.P_DIRECT, mx.SCALE_UOS, True),
+    (mx.P_POSTNORM, mx.SCALE_UOS, True),  # materialized-P diagnostic (Sec. 5.5.2)
+    (mx.P_POSTNORM, mx.SCALE_OCP, False),
+    (mx.P_PNQ, mx.SCALE_UOS, False),      # rotation off
+])
+@pytest.mark.parametrize("cid", [1, 5])
+def test_reference_modes_match_oracle(cid, p_mode, rule, rotate):
+    w = W.WORKLOADS[cid]
+    B, H, N, d = w.shape
+    say(f"reference modes: workload {cid} p_mode={p_mode} rule={rule} rotate={rotate}")
+    bits = {t: W.generate(w, t) for t in "qkv"}
+    dev = {t: to_device(bits[t], w.dtype) for t in "qkv"}
+    sums = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    out = mx.quantize_reference_modes(dev["q"], dev["k"], dev["v"], rule=rule, p_mode=p_mode, rotate=rotate,
+                                      causal=w.causal, row_sums=sums)
+    torch.cuda.synchronize()
+    if cid == 1:
+        heads = [(0, 0), (0, 1)]
+        rows = np.arange(N, dtype=np.int32)
+    else:
+        heads = [(0, 0), (7, 9)]
+        rows = _sample_rows(N, 40, 5)
+    ref = _oracle_heads(w, heads, rows, p_mode=p_mode, rule=rule, rotate=rotate, bits=bits)
+    check_output(_gpu_rows(out, heads, rows), ref, f"workload {cid} mode {p_mode}/{rule}/{rotate}",
+                 (N + KV_TILE - 1) // KV_TILE)
+    rs = _gpu_rows(sums, heads, rows)
+    if p_mode == mx.P_PNQ:
+        assert np.abs(rs - 1).max() < 1e-5  # Prop. 1 on the GPU
+    else:
+        # rows whose result is not unique (a decision within DELTA of a
+        # boundary that moves the output by more than ABS_TOL) are excluded
+        unique = ref["amb"].max(axis=-1) <= 1e-2
+        assert np.allclose(rs[unique], ref["rowsum"][unique], rtol=2e-4, atol=2e-4)
+        say(f"  row sums compared on {int(unique.sum())}/{unique.size} rows")
+    say(f"  induced row sums: gpu mean {rs.mean():.5f} [{rs.min():.4f}, {rs.max():.4f}] "
+        f"oracle mean {ref['rowsum'].mean():.5f}")
+    # the PNQ-through-reference-modes path equals quantize x3 + forward bit for bit
+    if p_mode == mx.P_PNQ and rule == mx.SCALE_UOS and rotate:
+        direct_out, _ = run_forward(dev["q"], dev["k"], dev["v"], w.causal, with_stats=False)
+        assert torch.equal(direct_out, out)
+
+
+@pytest.mark.parametrize("N", [1, 2, 31, 127, 128, 129, 200, 300])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_and_tiny_shapes(N, d, causal):
+    say(f"forward ragged N={N} d={d} causal={causal}")
+    B, H = 2, 2
+    x = W.custom(B, H, N, d, seed=N + d, scale=2.0)
+    dev = {t: to_device(x[t], W.BF16) for t in "qkv"}
+    out, stats = run_forward(dev["q"], dev["k"], dev["v"], causal)
+    ref = oracle.attention(x["q"], x["k"], x["v"], W.BF16, B, H, N, d, causal=causal, kv_tile=KV_TILE,
+                           amb_delta=DELTA)
+    check_output(out.cpu().numpy(), ref, f"N={N} d={d} causal={causal}", (N + KV_TILE - 1) // KV_TILE)
+    assert (stats.cpu().numpy()[..., 1] >= 1.0).all()
+
+
+def test_fp16_inputs():
+    w = W.WORKLOADS[1]
+    assert w.dtype == W.FP16
+    x = W.custom(1, 3, 500, 128, dtype=W.FP16, seed=3, scale=2.0)
+    dev = {t: to_device(x[t], W.FP16) for t in "qkv"}
+    say("forward fp16 inputs")
+    out, _ = run_forward(dev["q"], dev["k"], dev["v"], False)
+    ref = oracle.attention(x["q"], x["k"], x["v"], W.FP16, 1, 3, 500, 128, amb_delta=DELTA)
+    check_output(out.cpu().numpy(), ref, "fp16", 4)
+
+
+# ----------------------------------------------------------------------------
+# invariants that need no oracle
+
+
+def test_constant_values_give_their_quantized_value_exactly():
+    """PNQ normalizes by the same quantized weights it aggregates with (Prop. 1):
+    with V constant per channel, O = Q*(c) for any Q and K.  Powers of two
+    quantize to themselves, so the output must equal them bit for bit.  The
+    logits are kept moderate so that no quantized weight falls into the
+    binary32 subnormal range, where the matrix core may flush terms of O~ and
+    of l differently."""
+    for causal in (False, True):
+        B, H, N, d = 2, 3, 700, 128
+        x = W.custom(B, H, N, d, seed=9, scale=0.7)
+        rng = np.random.default_rng(1)
+        c = np.exp2(rng.integers(-6, 6, d)) * rng.choice([-1.0, 1.0], d)
+        v = np.broadcast_to(W.to_bits(c, W.BF16), (B, H, N, d)).copy()
+        say(f"constant V causal={causal}")
+        out, stats = run_forward(to_device(x["q"], W.BF16), to_device(x["k"], W.BF16), to_device(v, W.BF16), causal)
+        o = out.cpu().numpy()
+        assert (o == c.astype(np.float32)[None, None, None, :]).all()
+
+
+def test_zero_queries_average_the_values():
+    """Q = 0: every score is 0, every P~ = 1 = P^, so O is the mean of V^ over
+    the visible keys (computed here from the GPU's own V^ codes)."""
+    B, H, N, d = 1, 2, 333, 128
+    x = W.custom(B, H, N, d, seed=10)
+    zq = np.zeros_like(x["q"])
+    dv = to_device(x["v"], W.BF16)
+    out, _ = run_forward(to_device(zq, W.BF16), to_device(x["k"], W.BF16), dv, False)
+    vm = mx.rotate_quantize(dv, mx.AXIS_TOKEN, rotate=False)
+    codes, scales = mx.unpack_tokens(vm)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    vals = grid[codes & 7] * np.where(codes & 8, -1.0, 1.0) * np.exp2(scales.astype(np.float64) - 127)[..., None]
+    vhat = vals.transpose(0, 1, 2, 4, 3).reshape(B, H, -1, d)[:, :, :N]
+    mean = vhat.mean(axis=2)
+    o = out.cpu().numpy().astype(np.float64)
+    say("zero queries")
+    assert np.allclose(o, mean[:, :, None, :], rtol=1e-5, atol=1e-6)
+
+
+def test_single_key_and_first_causal_row_copy_v():
+    B, H, d = 1, 2, 128
+    for N, causal in ((1, False), (260, True)):
+        x = W.custom(B, H, N, d, seed=11)
+        dv = to_device(x["v"], W.BF16)
+        out, _ = run_forward(to_device(x["q"], W.BF16), to_device(x["k"], W.BF16), dv, causal)
+        vm = mx.rotate_quantize(dv, mx.AXIS_TOKEN, rotate=False)
+        codes, scales = mx.unpack_tokens(vm)
+        grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+        v0 = grid[codes[:, :, 0, :, 0] & 7] * np.where(codes[:, :, 0, :, 0] & 8, -1.0, 1.0) * \
+            np.exp2(scales[:, :, 0].astype(np.float64) - 127)
+        assert (out.cpu().numpy()[:, :, 0] == v0.astype(np.float32)).all()
+
+
+def test_causal_leakage_on_gpu():
+    """The MatX block analysis on the GPU path: perturbing V at token j leaves
+    rows below its 32-token block bit-identical and changes rows of the block
+    before j; perturbing K at j leaves every row i < j bit-identical."""
+    B, H, N, d = 1, 2, 400, 128
+    x = W.custom(B, H, N, d, seed=12)
+    dq, dk = to_device(x["q"], W.BF16), to_device(x["k"], W.BF16)
+    base, _ = run_forward(dq, dk, to_device(x["v"], W.BF16), True)
+    for j in (45, 200, 399):
+        v = x["v"].copy()
+        v[:, :, j] = W.to_bits(W.from_bits(v[:, :, j], W.BF16).astype(np.float64) * 256.0, W.BF16)
+        o, _ = run_forward(dq, dk, to_device(v, W.BF16), True)
+        blk0 = 32 * (j // 32)
+        assert torch.equal(o[:, :, :blk0], base[:, :, :blk0])
+        assert (o[:, :, blk0:j] != base[:, :, blk0:j]).any(dim=-1).all()
+        k = x["k"].copy()
+        k[:, :, j] = W.to_bits(W.from_bits(k[:, :, j], W.BF16).astype(np.float64) * -5.0, W.BF16)
+        o2, _ = run_forward(dq, to_device(k, W.BF16), to_device(x["v"], W.BF16), True)
+        assert torch.equal(o2[:, :, :j], base[:, :, :j])
+        say(f"causal leakage j={j}: rows < {blk0} identical, rows {blk0}..{j - 1} changed")
+
+
+def test_forward_is_deterministic():
+    w = W.WORKLOADS[1]
+    dev = {t: to_device(W.generate(w, t), w.dtype) for t in "qkv"}
+    a, sa = run_forward(dev["q"], dev["k"], dev["v"], False)
+    b, sb = run_forward(dev["q"], dev["k"], dev["v"], False)
+    assert torch.equal(a, b) and torch.equal(sa, sb)

@@ -1,0 +1,169 @@
+"""GPU parity of the MXFP4 quantizers (HIP kernels through the C ABI) with the
+CPU oracle: codes and E8M0 scales must match bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_microscaled_bit_amd as mx
+import oracle
+import workloads as W
+from parity import compare_headdim, compare_tokens, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _rows_sample(B, H, N, n_random, seed, full_heads=((0, 0),)):
+    rng = np.random.default_rng(seed)
+    rows = set()
+    for b, h in full_heads:
+        rows.update(((b * H + h) * N + np.arange(N)).tolist())
+    rows.update(rng.integers(0, B * H * N, n_random).tolist())
+    for bh in (0, B * H - 1):  # head boundaries and the ragged tail
+        rows.update([bh * N, bh * N + N - 1])
+    return np.array(sorted(rows), np.int64)
+
+
+def _blocks_sample(B, H, N, n_random, seed):
+    NB = (N + 31) // 32
+    rng = np.random.default_rng(seed)
+    blocks = set(rng.integers(0, B * H * NB, n_random).tolist())
+    blocks.update([0, NB - 1, B * H * NB - 1, (B * H - 1) * NB])
+    return np.array(sorted(blocks), np.int64)
+
+
+@pytest.mark.parametrize("cid", [1, 5, 2, 4, 3])
+def test_workload_quantizers_bit_exact(cid):
+    w = W.WORKLOADS[cid]
+    B, H, N, d = w.shape
+    say(f"quantizer parity: workload {cid} {w.describe()}")
+    full = cid in (1, 5)
+    for t in ("q", "k", "v"):
+        bits = W.generate(w, t)
+        dev = to_device(bits, w.dtype)
+        if t in ("q", "k"):
+            rows = None if full else _rows_sample(B, H, N, 20000, cid)
+            rules = (mx.SCALE_UOS, mx.SCALE_OCP) if cid in (1, 5) else (mx.SCALE_UOS,)
+            for rule in rules:
+                for rotate in ((True, False) if cid == 1 else (True,)):
+                    bc, bs, n = compare_headdim(bits, w.dtype, B, H, N, d, rotate, rule, rows=rows, dev=dev)
+                    say(f"  {t} rotate={rotate} rule={rule}: {n} codes, mismatched codes {bc}, scales {bs}")
+                    assert bc == 0 and bs == 0
+        else:
+            blocks = None if full else _blocks_sample(B, H, N, 4000, cid)
+            for rule in ((mx.SCALE_UOS, mx.SCALE_OCP) if cid in (1, 5) else (mx.SCALE_UOS,)):
+                bc, bs, n = compare_tokens(bits, w.dtype, B, H, N, d, rule, blocks=blocks, dev=dev)
+                say(f"  v rule={rule}: {n} codes, mismatched codes {bc}, scales {bs}")
+                assert bc == 0 and bs == 0
+        del dev
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("N", [1, 31, 33, 127, 129, 200])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
+def test_ragged_shapes(N, d, dtype):
+    say(f"quantizer ragged N={N} d={d} dtype={dtype}")
+    x = W.custom(2, 3, N, d, dtype=dtype, seed=N * d, scale=3.0)
+    for rotate in (True, False):
+        for rule in (mx.SCALE_UOS, mx.SCALE_OCP):
+            bc, bs, _ = compare_headdim(x["q"], dtype, 2, 3, N, d, rotate, rule)
+            assert bc == 0 and bs == 0, (rotate, rule)
+    for rule in (mx.SCALE_UOS, mx.SCALE_OCP):
+        bc, bs, _ = compare_tokens(x["v"], dtype, 2, 3, N, d, rule)
+        assert bc == 0 and bs == 0, rule
+
+
+def _special_bits(N, d, dtype, seed):
+    """Inputs full of edge values: zeros of both signs, subnormals, exact
+    E2M1 ties after scaling, UOS/OCP boundary maxima, huge values."""
+    rng = np.random.default_rng(seed)
+    specials = np.array([0.0, -0.0, 1.0, -1.0, 14.5, 7.25, 3.625, 2.5, 5.0, 0.75, 1.75, 0.25, 6.0, 7.0,
+                         3.5, 1.25, 12.0, -12.0, 1e-38, -1e-39, 6e-8, 3e4, -65000.0, 2.0 ** -126, 2.0 ** -133,
+                         1e30, -3e38, 0.5 * 29 / 16 * 2, 29.0, 58.0, 0.453125])
+    if dtype == W.FP16:
+        specials = specials[np.abs(specials) < 65000]
+    vals = rng.choice(specials, size=(1, 2, N, d))
+    scale_pow = rng.integers(-20, 20, size=(1, 2, N, 1)).astype(np.float64)
+    if dtype == W.FP16:
+        scale_pow = np.clip(scale_pow, -4, 4)
+    vals = vals * np.exp2(scale_pow)
+    lim = 6.0e4 if dtype == W.FP16 else 1.0e37  # keep every input finite
+    vals = np.clip(vals, -lim, lim)
+    zero_rows = rng.random((1, 2, N)) < 0.1
+    vals[zero_rows] = 0.0
+    return W.to_bits(vals, dtype)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
+@pytest.mark.parametrize("d", [64, 128])
+def test_special_values(dtype, d):
+    N = 300
+    say(f"quantizer special values d={d} dtype={dtype}")
+    bits = _special_bits(N, d, dtype, seed=d + dtype)
+    for rotate in (True, False):
+        for rule in (mx.SCALE_UOS, mx.SCALE_OCP):
+            bc, bs, _ = compare_headdim(bits, dtype, 1, 2, N, d, rotate, rule)
+            assert bc == 0 and bs == 0, (rotate, rule)
+    for rule in (mx.SCALE_UOS, mx.SCALE_OCP):
+        bc, bs, _ = compare_tokens(bits, dtype, 1, 2, N, d, rule)
+        assert bc == 0 and bs == 0, rule
+
+
+def test_every_bf16_value_through_the_element_rounding():
+    """All finite bf16 values of magnitude <= 4 as V tokens next to a block
+    maximum of 4, 8 or 2 (exponent 0, +1, -1 under both rules), so every
+    value goes through the E2M1 rounding at three scales."""
+    say("quantizer exhaustive bf16 values")
+    allbits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    vals = W.from_bits(allbits, W.BF16).astype(np.float64)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 4.0)]
+    per_block = 31
+    nblk = (vals.size + per_block - 1) // per_block
+    flat = np.zeros(nblk * per_block)
+    flat[:vals.size] = vals
+    base = np.zeros((nblk, 32))
+    base[:, :per_block] = flat.reshape(nblk, per_block)
+    blocks = []
+    for mmax in (4.0, 8.0, 2.0):
+        b = base.copy()
+        b[:, 31] = mmax
+        blocks.append(b)
+    blocks = np.concatenate(blocks)                 # [nb, 32]
+    d = 128
+    nkb = (blocks.shape[0] + d - 1) // d
+    grid = np.zeros((nkb * d, 32))
+    grid[:blocks.shape[0]] = blocks
+    # channel c of token block kb carries block kb*d + c
+    v = grid.reshape(nkb, d, 32).transpose(0, 2, 1).reshape(1, 1, nkb * 32, d)
+    bits = W.to_bits(v, W.BF16)
+    assert (W.from_bits(bits, W.BF16) == v).all()
+    for rule in (mx.SCALE_UOS, mx.SCALE_OCP):
+        bc, bs, n = compare_tokens(bits, W.BF16, 1, 1, nkb * 32, d, rule)
+        say(f"  rule={rule}: {n} codes, mismatched {bc}/{bs}")
+        assert bc == 0 and bs == 0
+
+
+def test_strided_input_layout():
+    """A [B, N, H, d] buffer viewed as [B, H, N, d] (no copy) quantizes like the
+    contiguous tensor."""
+    B, H, N, d = 2, 3, 150, 128
+    x = W.custom(B, N, H, d, seed=77, tensors=("q",))["q"]  # physical [B, N, H, d]
+    dev = to_device(x, W.BF16).permute(0, 2, 1, 3)              # logical [B, H, N, d]
+    contig = np.ascontiguousarray(x.transpose(0, 2, 1, 3))
+    say("quantizer strided input")
+    for axis in (mx.AXIS_HEAD_DIM, mx.AXIS_TOKEN):
+        a = mx.rotate_quantize(dev, axis, rotate=(axis == mx.AXIS_HEAD_DIM))
+        b = mx.rotate_quantize(to_device(contig, W.BF16), axis, rotate=(axis == mx.AXIS_HEAD_DIM))
+        torch.cuda.synchronize()
+        assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+    bc, bs, _ = compare_headdim(contig, W.BF16, B, H, N, d, True, mx.SCALE_UOS)
+    assert bc == 0 and bs == 0
+
+
+def test_quantizer_is_deterministic():
+    w = W.WORKLOADS[1]
+    dev = to_device(W.generate(w, "q"), w.dtype)
+    a = mx.rotate_quantize(dev, mx.AXIS_HEAD_DIM)
+    b = mx.rotate_quantize(dev, mx.AXIS_HEAD_DIM)
+    torch.cuda.synchronize()
+    assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)

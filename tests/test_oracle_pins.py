@@ -629,3 +629,15 @@ def test_decision_allowance_is_nonnegative_and_off_by_default():
     r1 = oracle.attention(q, k, v, w.dtype, w.B, w.H, w.N, w.d, amb_delta=1e-3)
     assert (r1["amb"] >= 0).all() and r1["amb"].max() > 0
     assert (r1["out"] == r0["out"]).all()
+
+
+def test_absmass_equals_output_for_nonnegative_values():
+    """absmass is the output with |V^| in place of V^: for V >= 0 they coincide."""
+    N, d = 150, 64
+    x = W.custom(1, 1, N, d, seed=41, scale=2.0)
+    vpos = W.to_bits(np.abs(W.from_bits(x["v"], W.BF16).astype(np.float64)), W.BF16)
+    for mode in (oracle.P_PNQ, oracle.P_DIRECT, oracle.P_POSTNORM):
+        r = oracle.attention(x["q"], x["k"], vpos, W.BF16, 1, 1, N, d, p_mode=mode)
+        assert np.allclose(r["absmass"], r["out"], rtol=1e-14, atol=0)
+        r2 = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, p_mode=mode)
+        assert (r2["absmass"] >= np.abs(r2["out"]) * (1 - 1e-14)).all()
