@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Benchmark of MXAttention's MXFP4 attention forward on one MI355X.
+
+One step is the whole hot path on the Wan-like video self-attention shape
+(B=1, H=40, N=32760, d=128, bf16 inputs already in HBM):
+  rotate + UOS-quantize Q, rotate + UOS-quantize K, UOS-quantize V along
+  tokens, fused forward (scaled-FP4 QK^T, online softmax with PNQ,
+  scaled-FP4 PV).
+
+Prints one JSON line.  `value` is whole-step throughput in TFLOPS, counting
+4*B*H*N^2*d algorithmic flops (2*d per (query, key) pair for QK^T and as many
+for PV).  `roofline` describes the dominant kernel (the fused forward) against
+the dense MXFP4 matrix-core peak; its duration comes from HIP events recorded
+around each forward launch on the launch stream.  `cpu_baseline` times the
+plain CPU oracle on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_FP4_PEAK_TFLOPS = 10100.0  # MI355X dense MXFP4 matrix-core peak
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E peak
+QUANT_BYTES_PER_ELEMENT = 2.0 + 0.5 + 1.0 / 32.0  # bf16 in, E2M1 codes + E8M0 scales out
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_wan_like_traffic.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "mxfp4_microscaled_bit_amd", "csrc", "attention.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(launch_bytes_algorithmic: float):
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary, or None if there is none or the kernel changed since."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith("#"):
+                k, v = ln.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, target_s: float = 12.0):
+    """The CPU oracle on a bounded sample: two heads of the workload, a number
+    of query rows each against all N keys, sized to about target_s seconds."""
+    import numpy as np
+    import oracle
+    import workloads as W
+
+    heads = [(0, 0), (0, w.H // 2)]
+    sel = {t: W.generate(w, t, heads=heads)[None] for t in "qkv"}
+    nth = oracle.default_threads()
+
+    def run(n_rows):
+        rows = np.linspace(0, w.N - 1, n_rows).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.attention(sel["q"], sel["k"], sel["v"], w.dtype, 1, len(heads), w.N, w.d,
+                         causal=w.causal, kv_tile=128, rows=rows, nthreads=nth)
+        return time.perf_counter() - t0
+
+    # grow the row count until one run takes about target_s (the per-head
+    # quantization inside each call is a fixed cost, so scale from the last run)
+    n_rows = 2 * nth
+    t = run(n_rows)
+    while t < target_s / 3 and n_rows < w.N:
+        n_rows = int(min(w.N, max(2 * n_rows, n_rows * target_s / max(t, 1e-3))))
+        t = run(n_rows)
+    pairs = len(heads) * n_rows * w.N  # non-causal: every row sees every key
+    flops = 4.0 * w.d * pairs
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOPS",
+        "cores": nth,
+        "kind": "oracle",
+        "seconds": round(t, 3),
+        "sample": (f"{len(heads)} heads x {n_rows} query rows x all {w.N} keys of {w.name} "
+                   f"({w.describe()}), including the oracle's own quantization of those heads; "
+                   f"flops counted as 4*d per (query, key) pair"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="run three plain device-to-device copies of BYTES bytes and exit "
+                         "(reference kernel for scaling the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "(batch, head) with no communication, so per-GPU throughput is the one-GPU value.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mxfp4_microscaled_bit_amd as mx
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    if args.copy_probe:
+        n = args.copy_probe // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+        return
+
+    w = W.WORKLOADS[args.workload]
+    B, H, N, d = w.shape
+    log(f"workload {args.workload}: {w.name} {w.describe()}; generating inputs")
+    t0 = time.perf_counter()
+    dev = {}
+    for t in "qkv":
+        bits = W.generate(w, t)
+        ten = torch.from_numpy(bits.view("int16")).view(torch.bfloat16 if w.dtype == W.BF16 else torch.float16)
+        dev[t] = ten.cuda()
+        del bits
+    log(f"inputs resident in HBM after {time.perf_counter() - t0:.1f}s")
+
+    stream = torch.cuda.current_stream()
+    qm = mx.MXTensor.empty(B, H, N, d, mx.AXIS_HEAD_DIM)
+    km = mx.MXTensor.empty(B, H, N, d, mx.AXIS_HEAD_DIM)
+    vm = mx.MXTensor.empty(B, H, N, d, mx.AXIS_TOKEN)
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(record=None):
+        e = [ev() for _ in range(3)] if record is not None else None
+        if e:
+            e[0].record(stream)
+        mx.rotate_quantize(dev["q"], mx.AXIS_HEAD_DIM, rotate=True, out=qm)
+        mx.rotate_quantize(dev["k"], mx.AXIS_HEAD_DIM, rotate=True, out=km)
+        mx.rotate_quantize(dev["v"], mx.AXIS_TOKEN, rotate=False, out=vm)
+        if e:
+            e[1].record(stream)
+        mx.forward(qm, km, vm, causal=w.causal, out=out)
+        if e:
+            e[2].record(stream)
+            record.append(e)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / len(events)
+    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / len(events)
+    ms_per_step = wall * 1000.0 / args.steps
+    flops = w.flops()
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
+    quant_bytes = 3 * B * H * N * d * QUANT_BYTES_PER_ELEMENT
+    quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+
+    result = {
+        "metric": "fused MXFP4 attention fwd TFLOPS (1 GPU) + % of MXFP4 MFMA peak; quantizer GB/s",
+        "value": round(value, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp4",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.describe()}, one step = rotate+quantize Q, K; quantize V; "
+                               f"fused PNQ forward", "B": B, "H": H, "N": N, "d": d,
+                   "causal": w.causal, "kv_tile": mx.forward_kv_tile(d, w.causal)},
+        "forward": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
+                    "frac_mfma_peak": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4)},
+        "quantizer": {"ms": round(quant_ms, 4), "gb_per_s": round(quant_gbs, 1),
+                      "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
+                      "bytes": quant_bytes},
+        "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(flops)},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        result["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
