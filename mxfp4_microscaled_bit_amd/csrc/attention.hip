@@ -79,58 +79,87 @@ __device__ __forceinline__ int kc_granule(int k, int c) {
   else return (2 * k + c) ^ ((k >> 5) & 1) ^ (((k >> 6) & 1) << 3);
 }
 
+// (key, d-chunk) held by LDS granule G of the K^ stage (the inverse of kc_granule)
 template <int D>
-struct StageRegs {
-  static constexpr int KCU = (kBc * D / 2 / 16) / 256;  // uint4 per thread
-  static constexpr int VCU = (64 * D / 16) / 256;
-  uint4 kc[KCU];
-  uint4 vc[VCU];
+__device__ __forceinline__ int kc_source_chunk(int G) {
+  if constexpr (D == 128) {
+    const int k = G >> 2;
+    return 4 * k + ((G & 3) ^ ((k >> 5) & 3) ^ (k & 2));
+  } else {
+    const int g0 = (G >> 6) & 1, g1 = (G >> 7) & 1;
+    return G ^ g0 ^ (g1 << 3);  // = 2k + c
+  }
+}
+
+// Stage one key/value tile into LDS.  The code bytes (16 KB at d = 128) go
+// straight from global memory into LDS with global_load_lds_dwordx4: lane i
+// of a wave writes LDS granule base + i, so each lane fetches the global
+// 16-byte chunk that belongs in that (swizzled) granule.  The scale bytes are
+// few; they pass through registers and are scattered into their operand
+// order with byte stores (scale_store).
+// LDS-destination copy of one 16-byte chunk per lane (device code only: the
+// builtin takes an LDS address-space pointer, which the host pass cannot form)
+__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_base) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
+                                            reinterpret_cast<uintptr_t>(lds_base)),
+                                   16, 0, 0);
+#endif
+}
+
+template <int D>
+__device__ __forceinline__ void codes_dma(const Params& p, int64_t bh, int kt, uint8_t* stage, int tid) {
+  using L = Lds<D>;
+  constexpr int KG = kBc * D / 2 / 16;  // K^ granules per tile
+  constexpr int VG = 64 * D / 16;       // V^ granules per tile
+  const int NBp = p.Np / 32;
+  const int wave = tid >> 6, lane = tid & 63;
+  const uint8_t* kb = p.kc + (bh * p.Np + (int64_t)kt * kBc) * (D / 2);
+  const uint8_t* vb = p.vc + (bh * NBp + (int64_t)kt * 4) * D * 16;
+#pragma unroll
+  for (int u = 0; u < KG / 256; ++u) {
+    const int G0 = u * 256 + wave * 64;
+    dma16(kb + 16 * kc_source_chunk<D>(G0 + lane), stage + L::KC + 16 * G0);
+  }
+#pragma unroll
+  for (int u = 0; u < VG / 256; ++u) {
+    const int G0 = u * 256 + wave * 64;
+    dma16(vb + 16 * (G0 + lane), stage + L::VC + 16 * G0);
+  }
+}
+
+struct ScaleRegs {
   uint32_t ks;
   uint32_t vs;
 };
 
 template <int D>
-__device__ __forceinline__ void stage_load(StageRegs<D>& st, const Params& p, int64_t bh, int kt, int tid) {
+__device__ __forceinline__ ScaleRegs scale_load(const Params& p, int64_t bh, int kt, int tid) {
   const int NBp = p.Np / 32;
-  const uint4* kb = reinterpret_cast<const uint4*>(p.kc + (bh * p.Np + (int64_t)kt * kBc) * (D / 2));
-#pragma unroll
-  for (int u = 0; u < StageRegs<D>::KCU; ++u) st.kc[u] = kb[tid + 256 * u];
-  const uint4* vb = reinterpret_cast<const uint4*>(p.vc + (bh * NBp + (int64_t)kt * 4) * D * 16);
-#pragma unroll
-  for (int u = 0; u < StageRegs<D>::VCU; ++u) st.vc[u] = vb[tid + 256 * u];
-  st.ks = 0;
-  st.vs = 0;
+  ScaleRegs r = {0u, 0u};
   if (tid < kBc) {
     const uint8_t* ksrc = p.ks + (bh * p.Np + (int64_t)kt * kBc + tid) * (D / 32);
-    if constexpr (D == 128) st.ks = *reinterpret_cast<const uint32_t*>(ksrc);
-    else st.ks = *reinterpret_cast<const uint16_t*>(ksrc);
+    if constexpr (D == 128) r.ks = *reinterpret_cast<const uint32_t*>(ksrc);
+    else r.ks = *reinterpret_cast<const uint16_t*>(ksrc);
   }
-  if (tid < D) st.vs = *reinterpret_cast<const uint32_t*>(p.vs + (bh * NBp + (int64_t)kt * 4) * D + 4 * tid);
+  if (tid < D) r.vs = *reinterpret_cast<const uint32_t*>(p.vs + (bh * NBp + (int64_t)kt * 4) * D + 4 * tid);
+  return r;
 }
 
 template <int D>
-__device__ __forceinline__ void stage_store(const StageRegs<D>& st, uint8_t* lds, int tid) {
+__device__ __forceinline__ void scale_store(const ScaleRegs& r, uint8_t* stage, int tid) {
   using L = Lds<D>;
-#pragma unroll
-  for (int u = 0; u < StageRegs<D>::KCU; ++u) {
-    const int idx = tid + 256 * u;
-    const int k = idx / (D / 32), c = idx % (D / 32);
-    *reinterpret_cast<uint4*>(lds + L::KC + 16 * kc_granule<D>(k, c)) = st.kc[u];
-  }
-#pragma unroll
-  for (int u = 0; u < StageRegs<D>::VCU; ++u)
-    *reinterpret_cast<uint4*>(lds + L::VC + 16 * (tid + 256 * u)) = st.vc[u];
   if (tid < kBc) {
-    const int k = tid, g = k >> 5, t = (k >> 2) & 7, i = k & 3, r = 4 * g + i;
+    const int k = tid, g = k >> 5, t = (k >> 2) & 7, i = k & 3, rr = 4 * g + i;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) lds[L::KS + (c * 16 + r) * 8 + t] = (uint8_t)(st.ks >> (8 * c));
+    for (int c = 0; c < D / 32; ++c) stage[L::KS + (c * 16 + rr) * 8 + t] = (uint8_t)(r.ks >> (8 * c));
   }
   if (tid < D) {
     const int g = (4 * tid) / D;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int ch = (4 * tid) % D + j, ct = ch / 16, r = ch % 16;
-      lds[L::VS + (g * 16 + r) * (D / 16) + ct] = (uint8_t)(st.vs >> (8 * j));
+      const int ch = (4 * tid) % D + j, ct = ch / 16, rr = ch % 16;
+      stage[L::VS + (g * 16 + rr) * (D / 16) + ct] = (uint8_t)(r.vs >> (8 * j));
     }
   }
 }
@@ -178,19 +207,174 @@ struct RowState {
   float l;    // DIRECT / STATS: running sum of unquantized exponentials
 };
 
-template <int D, bool CAUSAL, int MODE, int RULE>
-__global__ __launch_bounds__(256) void k_attention(Params p) {
-  using L = Lds<D>;
-  constexpr int NCT = D / 16;  // 16-channel output tiles
+template <int D, int MODE, int RULE>
+struct FwdConsts {
+  static constexpr int NCT = D / 16;  // 16-channel output tiles
   // Exponent arguments.  The fused path evaluates (s - m) c as one
   // fma(s, c, -m c); the row maximum then gives P~ = 1 within an ulp, which
   // the UOS rule maps to the interior value 4.  The OCP rule puts P~ = 1 on
   // its scale boundary (floor(log2 1) - 2), and the reference modes must
   // reproduce exact ties, so they evaluate fma(s - m, c, -off), which is
   // exact when s = m.
-  constexpr bool kExactArg = !(MODE == kModePnq && RULE == kRuleUos);
-  constexpr float kC = (D == 128) ? 0x1.0527dcp-3f : 0x1.715476p-3f;      // log2(e)/sqrt(d)
-  constexpr float kInvSqrtD = (D == 128) ? 0x1.6a09e6p-4f : 0x1p-3f;      // 1/sqrt(d)
+  static constexpr bool kExactArg = !(MODE == kModePnq && RULE == kRuleUos);
+  static constexpr float kC = (D == 128) ? 0x1.0527dcp-3f : 0x1.715476p-3f;  // log2(e)/sqrt(d)
+  static constexpr float kInvSqrtD = (D == 128) ? 0x1.6a09e6p-4f : 0x1p-3f;  // 1/sqrt(d)
+};
+
+// Online-softmax update and P^ of one 16-query sub-block for one key tile:
+// s holds the lane's 32 scores (one 32-key block of query L%16).  Returns the
+// packed FP4 B operand of the PV product; writes its E8M0 scale and alpha.
+template <int D, int MODE, int RULE>
+__device__ __forceinline__ uint4 softmax_block(v4f (&s)[8], RowState& rs, int& psc, float& alpha) {
+  using F = FwdConsts<D, MODE, RULE>;
+  float bmax = s[0][0];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[t][i]);
+  float a = 1.0f;
+  if constexpr (MODE != kModePostnorm) {
+    float rmax = fmaxf(bmax, xor_lanes(bmax, 16));
+    rmax = fmaxf(rmax, xor_lanes(rmax, 32));
+    const float m_new = fmaxf(rs.m, rmax);
+    if (m_new != -INFINITY) {
+      a = __builtin_amdgcn_exp2f((rs.m - m_new) * F::kC);  // 0 on the first visited tile
+      rs.m = m_new;
+      rs.mc = m_new * F::kC;
+    }
+  }
+  alpha = a;
+  const float mc = rs.mc, mref = rs.m, off = rs.off;
+  if constexpr (MODE == kModeStats) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f((s[t][i] - mref) * F::kC);
+    sum += xor_lanes(sum, 16);
+    sum += xor_lanes(sum, 32);
+    rs.l = a * rs.l + sum;
+    psc = 127;
+    return make_uint4(0, 0, 0, 0);
+  } else {
+    // block scale from the block max of the exponentials (exp is monotone)
+    const float Mb = F::kExactArg ? __builtin_amdgcn_exp2f(fmaf(bmax - mref, F::kC, -off))
+                                  : __builtin_amdgcn_exp2f(fmaf(bmax, F::kC, -mc));
+    const int e = scale_exponent<RULE>(Mb);
+    float y[32];
+    if constexpr (F::kExactArg) {
+      const float nb = -(off + (float)e);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[t][i] - mref, F::kC, nb));
+    } else {
+      const float nb = -(mc + (float)e);
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], F::kC, nb));
+    }
+    if constexpr (MODE == kModeDirect) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) sum += y[k];
+      sum = __builtin_amdgcn_ldexpf(sum, e);
+      sum += xor_lanes(sum, 16);
+      sum += xor_lanes(sum, 32);
+      rs.l = a * rs.l + sum;
+    }
+    psc = e + 127;
+    return make_uint4(pack_fp4x8(y), pack_fp4x8(y + 8), pack_fp4x8(y + 16), pack_fp4x8(y + 24));
+  }
+}
+
+// One key tile for the wave's 32 queries.  MASKED tiles (the ragged last tile
+// and the causal diagonal) set scores of invisible keys to -inf; every other
+// tile runs without any per-element test.
+template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
+__device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[2],
+                                          const int (&qsc)[2], const int (&qi)[2], RowState (&rs)[2],
+                                          v4f (&acc)[2][D / 16 + 1], int r16, int grp) {
+  using L = Lds<D>;
+  constexpr int NCT = D / 16;
+  // ---- S^T = K^ Q^T for 128 keys x 32 queries
+  uint2 ksw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  if (grp < D / 32) ksw = *reinterpret_cast<const uint2*>(buf + L::KS + (grp * 16 + r16) * 8);
+  v4f s0[8], s1[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const int k = 32 * (r16 >> 2) + 4 * t + (r16 & 3);
+    uint4 a = *reinterpret_cast<const uint4*>(buf + L::KC + 16 * kc_granule<D>(k, grp & (D / 32 - 1)));
+    if (D == 64 && grp >= 2) a = make_uint4(0, 0, 0, 0);
+    const int sc = (t < 4) ? (int)ksw.x : (int)ksw.y;
+    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+    switch (t & 3) {
+      case 0: s0[t] = mfma4<0>(a, qop[0], z, sc, qsc[0]); s1[t] = mfma4<0>(a, qop[1], z, sc, qsc[1]); break;
+      case 1: s0[t] = mfma4<1>(a, qop[0], z, sc, qsc[0]); s1[t] = mfma4<1>(a, qop[1], z, sc, qsc[1]); break;
+      case 2: s0[t] = mfma4<2>(a, qop[0], z, sc, qsc[0]); s1[t] = mfma4<2>(a, qop[1], z, sc, qsc[1]); break;
+      default: s0[t] = mfma4<3>(a, qop[0], z, sc, qsc[0]); s1[t] = mfma4<3>(a, qop[1], z, sc, qsc[1]); break;
+    }
+  }
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kt * kBc + 32 * grp + 4 * t + i;
+        if (!(key < N && (!CAUSAL || key <= qi[0]))) s0[t][i] = -INFINITY;
+        if (!(key < N && (!CAUSAL || key <= qi[1]))) s1[t][i] = -INFINITY;
+      }
+  }
+
+  // keep the V^ operand loads below the softmax: hoisting them above it
+  // would hold 32 more registers across the exponentials
+  __builtin_amdgcn_sched_barrier(0);
+  // ---- online softmax and P^ of both sub-blocks
+  int psc[2];
+  float alpha[2];
+  uint4 pq[2];
+  pq[0] = softmax_block<D, MODE, RULE>(s0, rs[0], psc[0], alpha[0]);
+  pq[1] = softmax_block<D, MODE, RULE>(s1, rs[1], psc[1], alpha[1]);
+
+  __builtin_amdgcn_sched_barrier(0);
+  if constexpr (MODE != kModeStats) {
+    // ---- rescale O~ (and the l column) only when some running max moved
+    if constexpr (MODE != kModePostnorm) {
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        if (__any(alpha[sb] != 1.0f)) {
+#pragma unroll
+          for (int ct = 0; ct <= NCT; ++ct) acc[sb][ct] *= alpha[sb];
+        }
+      }
+    }
+    // ---- O~ += P^ V^ and l += P^ 1
+    uint2 vsw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
+    if constexpr (D == 128) vsw = *reinterpret_cast<const uint2*>(buf + L::VS + (grp * 16 + r16) * 8);
+    else vsw.x = *reinterpret_cast<const uint32_t*>(buf + L::VS + (grp * 16 + r16) * 4);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const uint4 a = *reinterpret_cast<const uint4*>(buf + L::VC + 16 * (grp * D + 16 * ct + r16));
+      const int sc = (ct < 4) ? (int)vsw.x : (int)vsw.y;
+      switch (ct & 3) {
+        case 0: acc[0][ct] = mfma4<0>(a, pq[0], acc[0][ct], sc, psc[0]); acc[1][ct] = mfma4<0>(a, pq[1], acc[1][ct], sc, psc[1]); break;
+        case 1: acc[0][ct] = mfma4<1>(a, pq[0], acc[0][ct], sc, psc[0]); acc[1][ct] = mfma4<1>(a, pq[1], acc[1][ct], sc, psc[1]); break;
+        case 2: acc[0][ct] = mfma4<2>(a, pq[0], acc[0][ct], sc, psc[0]); acc[1][ct] = mfma4<2>(a, pq[1], acc[1][ct], sc, psc[1]); break;
+        default: acc[0][ct] = mfma4<3>(a, pq[0], acc[0][ct], sc, psc[0]); acc[1][ct] = mfma4<3>(a, pq[1], acc[1][ct], sc, psc[1]); break;
+      }
+    }
+    const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);  // E2M1 1.0
+    acc[0][NCT] = mfma4<0>(ones, pq[0], acc[0][NCT], 127, psc[0]);
+    acc[1][NCT] = mfma4<0>(ones, pq[1], acc[1][NCT], 127, psc[1]);
+  }
+}
+
+template <int D, bool CAUSAL, int MODE, int RULE>
+__global__ __launch_bounds__(256, 2) void k_attention(Params p) {
+  using L = Lds<D>;
+  using F = FwdConsts<D, MODE, RULE>;
+  constexpr int NCT = F::NCT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
 
   const int tid = threadIdx.x;
@@ -208,6 +392,8 @@ __global__ __launch_bounds__(256) void k_attention(Params p) {
   if (CAUSAL) qt = p.nqt - 1 - qt;  // longest causal rows first
   const int nkt_all = (p.N + kBc - 1) / kBc;
   const int nkt = CAUSAL ? min(qt + 1, nkt_all) : nkt_all;
+  // leading tiles in which every key is visible to every query of the tile
+  const int nfull = CAUSAL ? min(qt, nkt) : p.N / kBc;
 
   // Q^ operands of the two sub-blocks (B operand: lane = query L%16, d-chunk L/16)
   uint4 qop[2];
@@ -236,7 +422,7 @@ __global__ __launch_bounds__(256) void k_attention(Params p) {
       const float* st = p.stats + (bh * p.Np + qi[sb]) * 2;
       rs[sb].m = st[0];
       rs[sb].off = __builtin_amdgcn_logf(st[1]);  // log2 of l*
-      rs[sb].mc = st[0] * kC + rs[sb].off;
+      rs[sb].mc = st[0] * F::kC + rs[sb].off;
     }
   }
   v4f acc[2][NCT + 1];
@@ -245,156 +431,29 @@ __global__ __launch_bounds__(256) void k_attention(Params p) {
 #pragma unroll
     for (int ct = 0; ct <= NCT; ++ct) acc[sb][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-  StageRegs<D> st;
-  stage_load<D>(st, p, bh, 0, tid);
-  stage_store<D>(st, lds, tid);
+  codes_dma<D>(p, bh, 0, lds, tid);
+  scale_store<D>(scale_load<D>(p, bh, 0, tid), lds, tid);
+  __builtin_amdgcn_s_waitcnt(0);  // the DMA has landed in LDS
   __syncthreads();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    uint8_t* buf = lds + (kt & 1) * L::STAGE;
-    if (kt + 1 < nkt) stage_load<D>(st, p, bh, kt + 1, tid);
-
-    // ---- S^T = K^ Q^T for 128 keys x 32 queries
-    uint2 ksw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-    if (grp < D / 32) ksw = *reinterpret_cast<const uint2*>(buf + L::KS + (grp * 16 + r16) * 8);
-    v4f s[2][8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int k = 32 * (r16 >> 2) + 4 * t + (r16 & 3);
-      uint4 a = *reinterpret_cast<const uint4*>(buf + L::KC + 16 * kc_granule<D>(k, grp & (D / 32 - 1)));
-      if (grp >= D / 32) a = make_uint4(0, 0, 0, 0);
-      const int sc = (t < 4) ? (int)ksw.x : (int)ksw.y;
-      const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        switch (t & 3) {
-          case 0: s[sb][t] = mfma4<0>(a, qop[sb], z, sc, qsc[sb]); break;
-          case 1: s[sb][t] = mfma4<1>(a, qop[sb], z, sc, qsc[sb]); break;
-          case 2: s[sb][t] = mfma4<2>(a, qop[sb], z, sc, qsc[sb]); break;
-          default: s[sb][t] = mfma4<3>(a, qop[sb], z, sc, qsc[sb]); break;
-        }
-      }
-    }
-
-    // masks: keys past N (last tile) and keys after the query (causal diagonal)
-    const bool need_mask = (kt * kBc + kBc > p.N) || (CAUSAL && kt == qt);
-    if (need_mask) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt * kBc + 32 * grp + 4 * t + i;
-            const bool ok = key < p.N && (!CAUSAL || key <= qi[sb]);
-            if (!ok) s[sb][t][i] = -INFINITY;
-          }
-    }
-
-    // ---- online softmax and P^ per sub-block
-    uint4 pq[2];
-    int psc[2];
-    float alpha[2];
-#pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-      float bmax = s[sb][0][0];
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[sb][t][i]);
-      float a = 1.0f;
-      if constexpr (MODE != kModePostnorm) {
-        float rmax = fmaxf(bmax, xor_lanes(bmax, 16));
-        rmax = fmaxf(rmax, xor_lanes(rmax, 32));
-        const float m_new = fmaxf(rs[sb].m, rmax);
-        if (m_new != -INFINITY) {
-          a = __builtin_amdgcn_exp2f((rs[sb].m - m_new) * kC);  // 0 on the first visited tile
-          rs[sb].m = m_new;
-          rs[sb].mc = m_new * kC;
-        }
-      }
-      alpha[sb] = a;
-      const float mc = rs[sb].mc;
-      const float mref = rs[sb].m, off = rs[sb].off;
-      if constexpr (MODE == kModeStats) {
-        float sum = 0.0f;
-#pragma unroll
-        for (int t = 0; t < 8; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f((s[sb][t][i] - mref) * kC);
-        sum += xor_lanes(sum, 16);
-        sum += xor_lanes(sum, 32);
-        rs[sb].l = a * rs[sb].l + sum;
-        pq[sb] = make_uint4(0, 0, 0, 0);
-        psc[sb] = 127;
-      } else {
-        // block scale from the block max of the exponentials (exp is monotone)
-        const float Mb = kExactArg ? __builtin_amdgcn_exp2f(fmaf(bmax - mref, kC, -off))
-                                   : __builtin_amdgcn_exp2f(fmaf(bmax, kC, -mc));
-        const int e = scale_exponent<RULE>(Mb);
-        float y[32];
-        if constexpr (kExactArg) {
-          const float nb = -(off + (float)e);
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[sb][t][i] - mref, kC, nb));
-        } else {
-          const float nb = -(mc + (float)e);
-#pragma unroll
-          for (int t = 0; t < 8; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) y[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[sb][t][i], kC, nb));
-        }
-        if constexpr (MODE == kModeDirect) {
-          float sum = 0.0f;
-#pragma unroll
-          for (int k = 0; k < 32; ++k) sum += y[k];
-          sum = __builtin_amdgcn_ldexpf(sum, e);
-          sum += xor_lanes(sum, 16);
-          sum += xor_lanes(sum, 32);
-          rs[sb].l = a * rs[sb].l + sum;
-        }
-        pq[sb] = make_uint4(pack_fp4x8(y), pack_fp4x8(y + 8), pack_fp4x8(y + 16), pack_fp4x8(y + 24));
-        psc[sb] = e + 127;
-      }
-    }
-
-    if constexpr (MODE != kModeStats) {
-      // ---- rescale O~ (and the l column) when any running max moved
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        if (MODE != kModePostnorm && __any(alpha[sb] != 1.0f)) {
-#pragma unroll
-          for (int ct = 0; ct <= NCT; ++ct) acc[sb][ct] *= alpha[sb];
-        }
-      }
-      // ---- O~ += P^ V^ and l += P^ 1
-      uint2 vsw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-      if constexpr (D == 128) vsw = *reinterpret_cast<const uint2*>(buf + L::VS + (grp * 16 + r16) * 8);
-      else vsw.x = *reinterpret_cast<const uint32_t*>(buf + L::VS + (grp * 16 + r16) * 4);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const uint4 a = *reinterpret_cast<const uint4*>(buf + L::VC + 16 * (grp * D + 16 * ct + r16));
-        const int sc = (ct < 4) ? (int)vsw.x : (int)vsw.y;
-#pragma unroll
-        for (int sb = 0; sb < 2; ++sb) {
-          switch (ct & 3) {
-            case 0: acc[sb][ct] = mfma4<0>(a, pq[sb], acc[sb][ct], sc, psc[sb]); break;
-            case 1: acc[sb][ct] = mfma4<1>(a, pq[sb], acc[sb][ct], sc, psc[sb]); break;
-            case 2: acc[sb][ct] = mfma4<2>(a, pq[sb], acc[sb][ct], sc, psc[sb]); break;
-            default: acc[sb][ct] = mfma4<3>(a, pq[sb], acc[sb][ct], sc, psc[sb]); break;
-          }
-        }
-      }
-      const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);  // E2M1 1.0
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) acc[sb][NCT] = mfma4<0>(ones, pq[sb], acc[sb][NCT], 127, psc[sb]);
-    }
-
-    if (kt + 1 < nkt) stage_store<D>(st, lds + ((kt + 1) & 1) * L::STAGE, tid);
+  // full tiles: no per-element masking; the next tile is copied into the
+  // other buffer while this one is processed (on the last iteration the
+  // clamped index copies this tile again into a buffer nothing reads later)
+  for (int kt = 0; kt < nfull; ++kt) {
+    const uint8_t* buf = lds + (kt & 1) * L::STAGE;
+    uint8_t* nxt = lds + ((kt + 1) & 1) * L::STAGE;
+    const int kn = min(kt + 1, nkt - 1);
+    codes_dma<D>(p, bh, kn, nxt, tid);
+    const ScaleRegs sr = scale_load<D>(p, bh, kn, tid);
+    tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, rs, acc, r16, grp);
+    scale_store<D>(sr, nxt, tid);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  // at most one masked tile: the ragged end of the keys or the causal diagonal
+  if (nfull < nkt)
+    tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, rs, acc,
+                                           r16, grp);
 
   // ---- epilogue
 #pragma unroll
@@ -424,7 +483,7 @@ __global__ __launch_bounds__(256) void k_attention(Params p) {
     }
     if (grp == 0) {
       if (p.row_stats) {
-        p.row_stats[(bh * p.N + q) * 2 + 0] = rs[sb].m * kInvSqrtD;
+        p.row_stats[(bh * p.N + q) * 2 + 0] = rs[sb].m * F::kInvSqrtD;
         p.row_stats[(bh * p.N + q) * 2 + 1] = l;
       }
       if (p.row_sums) p.row_sums[bh * p.N + q] = (MODE == kModePostnorm) ? lsum : lsum / l;
