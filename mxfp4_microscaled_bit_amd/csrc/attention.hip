@@ -289,9 +289,52 @@ __device__ __forceinline__ uint4 softmax_block(v4f (&s)[8], RowState& rs, int& p
   }
 }
 
-// One key tile for the wave's 32 queries.  MASKED tiles (the ragged last tile
-// and the causal diagonal) set scores of invisible keys to -inf; every other
-// tile runs without any per-element test.
+template <int D, bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void mask_scores(v4f (&s)[8], int kt, int N, int q, int grp) {
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kt * kBc + 32 * grp + 4 * t + i;
+        if (!(key < N && (!CAUSAL || key <= q))) s[t][i] = -INFINITY;
+      }
+  }
+}
+
+// O~ (and the l column) of one sub-block: rescale by alpha when a running
+// max moved, then accumulate P^ V^ and P^ 1 with the matrix cores.
+template <int D, int MODE>
+__device__ __forceinline__ void pv_block(const uint4 (&vop)[D / 16], uint2 vsw, uint4 pq, int psc, float alpha,
+                                         v4f (&acc)[D / 16 + 1]) {
+  constexpr int NCT = D / 16;
+  if constexpr (MODE != kModePostnorm) {
+    if (__any(alpha != 1.0f)) {
+#pragma unroll
+      for (int ct = 0; ct <= NCT; ++ct) acc[ct] *= alpha;
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int sc = (ct < 4) ? (int)vsw.x : (int)vsw.y;
+    switch (ct & 3) {
+      case 0: acc[ct] = mfma4<0>(vop[ct], pq, acc[ct], sc, psc); break;
+      case 1: acc[ct] = mfma4<1>(vop[ct], pq, acc[ct], sc, psc); break;
+      case 2: acc[ct] = mfma4<2>(vop[ct], pq, acc[ct], sc, psc); break;
+      default: acc[ct] = mfma4<3>(vop[ct], pq, acc[ct], sc, psc); break;
+    }
+  }
+  const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);  // E2M1 1.0
+  acc[NCT] = mfma4<0>(ones, pq, acc[NCT], 127, psc);
+}
+
+// One key tile for the wave's 32 queries, ordered so the matrix cores and the
+// vector ALU overlap inside the wave: both sub-blocks' S products are issued
+// first; the softmax of sub-block 0 runs while those of sub-block 1 are in
+// flight; its PV products are issued before the softmax of sub-block 1, which
+// then runs while they execute.  MASKED tiles (the ragged last tile and the
+// causal diagonal) set scores of invisible keys to -inf; every other tile runs
+// without any per-element test.
 template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
 __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[2],
                                           const int (&qsc)[2], const int (&qi)[2], RowState (&rs)[2],
@@ -301,72 +344,61 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   // ---- S^T = K^ Q^T for 128 keys x 32 queries
   uint2 ksw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
   if (grp < D / 32) ksw = *reinterpret_cast<const uint2*>(buf + L::KS + (grp * 16 + r16) * 8);
-  v4f s0[8], s1[8];
+  uint4 kop[8];
 #pragma unroll
   for (int t = 0; t < 8; ++t) {
     const int k = 32 * (r16 >> 2) + 4 * t + (r16 & 3);
-    uint4 a = *reinterpret_cast<const uint4*>(buf + L::KC + 16 * kc_granule<D>(k, grp & (D / 32 - 1)));
-    if (D == 64 && grp >= 2) a = make_uint4(0, 0, 0, 0);
-    const int sc = (t < 4) ? (int)ksw.x : (int)ksw.y;
-    const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-    switch (t & 3) {
-      case 0: s0[t] = mfma4<0>(a, qop[0], z, sc, qsc[0]); s1[t] = mfma4<0>(a, qop[1], z, sc, qsc[1]); break;
-      case 1: s0[t] = mfma4<1>(a, qop[0], z, sc, qsc[0]); s1[t] = mfma4<1>(a, qop[1], z, sc, qsc[1]); break;
-      case 2: s0[t] = mfma4<2>(a, qop[0], z, sc, qsc[0]); s1[t] = mfma4<2>(a, qop[1], z, sc, qsc[1]); break;
-      default: s0[t] = mfma4<3>(a, qop[0], z, sc, qsc[0]); s1[t] = mfma4<3>(a, qop[1], z, sc, qsc[1]); break;
+    kop[t] = *reinterpret_cast<const uint4*>(buf + L::KC + 16 * kc_granule<D>(k, grp & (D / 32 - 1)));
+    if (D == 64 && grp >= 2) kop[t] = make_uint4(0, 0, 0, 0);
+  }
+  v4f s0[8], s1[8];
+  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int sb = 0; sb < 2; ++sb) {
+    v4f (&s)[8] = sb ? s1 : s0;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const int sc = (t < 4) ? (int)ksw.x : (int)ksw.y;
+      switch (t & 3) {
+        case 0: s[t] = mfma4<0>(kop[t], qop[sb], z, sc, qsc[sb]); break;
+        case 1: s[t] = mfma4<1>(kop[t], qop[sb], z, sc, qsc[sb]); break;
+        case 2: s[t] = mfma4<2>(kop[t], qop[sb], z, sc, qsc[sb]); break;
+        default: s[t] = mfma4<3>(kop[t], qop[sb], z, sc, qsc[sb]); break;
+      }
     }
   }
-  if constexpr (MASKED) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt * kBc + 32 * grp + 4 * t + i;
-        if (!(key < N && (!CAUSAL || key <= qi[0]))) s0[t][i] = -INFINITY;
-        if (!(key < N && (!CAUSAL || key <= qi[1]))) s1[t][i] = -INFINITY;
-      }
-  }
-
-  // keep the V^ operand loads below the softmax: hoisting them above it
-  // would hold 32 more registers across the exponentials
   __builtin_amdgcn_sched_barrier(0);
-  // ---- online softmax and P^ of both sub-blocks
-  int psc[2];
-  float alpha[2];
-  uint4 pq[2];
-  pq[0] = softmax_block<D, MODE, RULE>(s0, rs[0], psc[0], alpha[0]);
-  pq[1] = softmax_block<D, MODE, RULE>(s1, rs[1], psc[1], alpha[1]);
 
+  // ---- sub-block 0: softmax and P^, while the S products of sub-block 1 run
+  mask_scores<D, CAUSAL, MASKED>(s0, kt, N, qi[0], grp);
+  int psc0;
+  float a0;
+  const uint4 pq0 = softmax_block<D, MODE, RULE>(s0, rs[0], psc0, a0);
   __builtin_amdgcn_sched_barrier(0);
+
   if constexpr (MODE != kModeStats) {
-    // ---- rescale O~ (and the l column) only when some running max moved
-    if constexpr (MODE != kModePostnorm) {
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        if (__any(alpha[sb] != 1.0f)) {
-#pragma unroll
-          for (int ct = 0; ct <= NCT; ++ct) acc[sb][ct] *= alpha[sb];
-        }
-      }
-    }
-    // ---- O~ += P^ V^ and l += P^ 1
     uint2 vsw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
     if constexpr (D == 128) vsw = *reinterpret_cast<const uint2*>(buf + L::VS + (grp * 16 + r16) * 8);
     else vsw.x = *reinterpret_cast<const uint32_t*>(buf + L::VS + (grp * 16 + r16) * 4);
+    uint4 vop[NCT];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const uint4 a = *reinterpret_cast<const uint4*>(buf + L::VC + 16 * (grp * D + 16 * ct + r16));
-      const int sc = (ct < 4) ? (int)vsw.x : (int)vsw.y;
-      switch (ct & 3) {
-        case 0: acc[0][ct] = mfma4<0>(a, pq[0], acc[0][ct], sc, psc[0]); acc[1][ct] = mfma4<0>(a, pq[1], acc[1][ct], sc, psc[1]); break;
-        case 1: acc[0][ct] = mfma4<1>(a, pq[0], acc[0][ct], sc, psc[0]); acc[1][ct] = mfma4<1>(a, pq[1], acc[1][ct], sc, psc[1]); break;
-        case 2: acc[0][ct] = mfma4<2>(a, pq[0], acc[0][ct], sc, psc[0]); acc[1][ct] = mfma4<2>(a, pq[1], acc[1][ct], sc, psc[1]); break;
-        default: acc[0][ct] = mfma4<3>(a, pq[0], acc[0][ct], sc, psc[0]); acc[1][ct] = mfma4<3>(a, pq[1], acc[1][ct], sc, psc[1]); break;
-      }
-    }
-    const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);  // E2M1 1.0
-    acc[0][NCT] = mfma4<0>(ones, pq[0], acc[0][NCT], 127, psc[0]);
-    acc[1][NCT] = mfma4<0>(ones, pq[1], acc[1][NCT], 127, psc[1]);
+    for (int ct = 0; ct < NCT; ++ct)
+      vop[ct] = *reinterpret_cast<const uint4*>(buf + L::VC + 16 * (grp * D + 16 * ct + r16));
+    pv_block<D, MODE>(vop, vsw, pq0, psc0, a0, acc[0]);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // ---- sub-block 1, while the PV products of sub-block 0 run
+    mask_scores<D, CAUSAL, MASKED>(s1, kt, N, qi[1], grp);
+    int psc1;
+    float a1;
+    const uint4 pq1 = softmax_block<D, MODE, RULE>(s1, rs[1], psc1, a1);
+    __builtin_amdgcn_sched_barrier(0);
+    pv_block<D, MODE>(vop, vsw, pq1, psc1, a1, acc[1]);
+  } else {
+    mask_scores<D, CAUSAL, MASKED>(s1, kt, N, qi[1], grp);
+    int psc1;
+    float a1;
+    (void)softmax_block<D, MODE, RULE>(s1, rs[1], psc1, a1);
   }
 }
 
