@@ -1,12 +1,13 @@
 // Fused MXFP4 attention forward of MXAttention for gfx950 (MI355X).
 //
 // One workgroup = 4 waves = 128 queries of one (batch, head); each wave owns
-// 32 queries as two 16-query sub-blocks.  Key/value tiles of B_c = 128 keys
-// are staged through LDS (double buffered) and visited in ascending order
-// (MXAttention paper, Alg. 2 steps 10-19):
+// 32 queries.  Key/value tiles of B_c = 128 keys are staged through LDS
+// (double buffered) and visited in ascending order (MXAttention paper,
+// Alg. 2, the loop over key/value tiles):
 //
-//   S^T  = K^ Q^T         scaled-FP4 MFMA 16x16x128, one per 16 keys x 16
-//                         queries (block scales along d ride in the MFMA)
+//   S^T  = K^ Q^T         scaled-FP4 MFMA 32x32x64: four 32-key x 32-query
+//                         sub-tiles, d/64 products each (block scales along d
+//                         ride in the MFMA)
 //   m    = max(m, rowmax) running max per query                  (Eq. 3)
 //   P~   = exp(S - m)     exponentials                           (Eq. 5)
 //   P^   = Q*(P~)         UOS quantization per 32-key block      (Eq. 44)
@@ -14,16 +15,24 @@
 //   O~   = a O~ + P^ V^   ... feeds both updates (PNQ)           (Eq. 48)
 //   O    = O~ / l                                                (Eq. 8)
 //
-// Register layouts follow the gfx950 scaled MFMA: in a 16x16x128 product,
-// lane L supplies row/column L%16 and the 32-element K-chunk L/16, and holds
-// D[4*(L/16)+i][L%16].  The A operand of S^T takes the keys in the permuted
-// order row r <- key 32*(r/4) + 4t + r%4 (t = 16-key sub-tile), so after the
-// eight S products lane L holds, for query L%16, the 32 consecutive keys
-// 32*(L/16) .. +31 -- exactly one 32-key quantization block, and exactly the
-// B-operand chunk of the PV product.  P^ therefore never moves between lanes;
-// its block maximum is lane-local.  l comes from one more MFMA against a tile
-// of ones, so l and O~ are updated from the same quantized tile by the same
-// instruction stream (the PNQ identity).
+// Register layouts follow the gfx950 scaled MFMA 32x32x64: lane L supplies
+// row/column L%32 and the 32-element K chunk L/32, and holds
+// D[8j + 4(L/32) + i][L%32] in accumulator element 4j+i.  The A operand of
+// sub-tile t of S^T takes its rows in the permuted key order
+//   row r <- key 64(t/2) + 32((r/4)%2) + 16(t%2) + 4(r/8) + r%4,
+// so that lane L (g = L/32) ends up with, for query L%32, the 32 consecutive
+// keys 32g..32g+31 in sub-tiles 0 and 1 and the keys 64+32g..64+32g+31 in
+// sub-tiles 2 and 3, each in ascending order.  Each is one 32-key
+// quantization block, and each is exactly the lane's B-operand chunk of one
+// 64-key step of the PV product: P^ never moves between lanes and its block
+// maximum is lane-local.  The two lanes L and L^32 that share a query
+// exchange their maxima with one v_permlane32_swap.
+//
+// l comes from a 16x16x128 MFMA of P^ against a 0/1 pattern: A row r takes
+// the K chunks whose parity equals (r/4)%2, which sums, for every column, the
+// two lanes that hold the same query, and lands l of query L%32 in all four
+// accumulator elements of lane L.  l and O~ are thus updated from the same
+// quantized tile by the same instruction stream (the PNQ identity).
 //
 // Scores stay in raw units (q^.k^); exp(s - m) is evaluated as
 // exp2(fma(s, c, -m c)) with c = log2(e)/sqrt(d), and the block scale 2^e is
@@ -39,6 +48,7 @@ namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBr = 128;       // queries per workgroup
 constexpr int kBc = kKvTile;   // keys per tile
@@ -64,31 +74,39 @@ struct Params {
 template <int D>
 struct Lds {
   static constexpr int KC = 0;                  // K^ codes, swizzled 16-byte granules
-  static constexpr int KS = KC + kBc * D / 2;   // K^ scales as [chunk][r][t]
-  static constexpr int VC = KS + kBc * D / 32;  // V^ codes [block][channel][16]
-  static constexpr int VS = VC + 64 * D;        // V^ scales as [block][r][ct]
-  static constexpr int STAGE = VS + 4 * D;
+  static constexpr int KS = KC + kBc * D / 2;   // K^ scales, [lane][sub-tile pair] dwords
+  static constexpr int VC = KS + 64 * 8;        // V^ codes [block][channel][16]
+  static constexpr int VS = VC + 64 * D;        // V^ scales, [lane][PV step] dwords
+  static constexpr int STAGE = VS + 64 * 8;
 };
 
-// 16-byte granule of (key k, d-chunk c) in the K^ stage.  The MFMA operand
-// read has 16 lanes of one chunk fetch keys 32g + 4t + i (g, i = 0..3); the
-// XOR spreads them over distinct bank groups for both 8- and 16-lane phases.
-template <int D>
-__device__ __forceinline__ int kc_granule(int k, int c) {
-  if constexpr (D == 128) return 4 * k + (c ^ ((k >> 5) & 3) ^ (k & 2));
-  else return (2 * k + c) ^ ((k >> 5) & 1) ^ (((k >> 6) & 1) << 3);
+// key (0..127 within the tile) on A-operand row r of S^T sub-tile t
+__device__ __forceinline__ int tile_key(int t, int r) {
+  return 64 * (t >> 1) + 32 * ((r >> 2) & 1) + 16 * (t & 1) + 4 * (r >> 3) + (r & 3);
 }
 
-// (key, d-chunk) held by LDS granule G of the K^ stage (the inverse of kc_granule)
+// K^ tile in LDS: key k's 16-byte d-chunk c sits in granule (d/32) k + (c ^ x(k)).
+// An operand read of one sub-tile has lanes 0..7 fetch keys b+{0..3} and
+// b+32+{0..3}, lanes 8..15 keys b+4+{0..3} and b+36+{0..3} (same chunk); the
+// XOR term makes both every 8-lane and every 16-lane group of such a read
+// touch distinct granules modulo 8 and modulo 16.
+template <int D>
+__device__ __forceinline__ int kc_swizzle(int k) {
+  if constexpr (D == 128) return (((k >> 1) ^ (k >> 2)) & 1) | (((k >> 5) & 1) << 1);
+  else return (k >> 5) & 1;
+}
+
+template <int D>
+__device__ __forceinline__ int kc_granule(int k, int c) {
+  return (D / 32) * k + (c ^ kc_swizzle<D>(k));
+}
+
+// (key, d-chunk) index (d/32) k + c held by LDS granule G (inverse of kc_granule)
 template <int D>
 __device__ __forceinline__ int kc_source_chunk(int G) {
-  if constexpr (D == 128) {
-    const int k = G >> 2;
-    return 4 * k + ((G & 3) ^ ((k >> 5) & 3) ^ (k & 2));
-  } else {
-    const int g0 = (G >> 6) & 1, g1 = (G >> 7) & 1;
-    return G ^ g0 ^ (g1 << 3);  // = 2k + c
-  }
+  constexpr int NC = D / 32;
+  const int k = G / NC;
+  return NC * k + ((G % NC) ^ kc_swizzle<D>(k));
 }
 
 // Stage one key/value tile into LDS.  The code bytes (16 KB at d = 128) go
@@ -96,7 +114,7 @@ __device__ __forceinline__ int kc_source_chunk(int G) {
 // of a wave writes LDS granule base + i, so each lane fetches the global
 // 16-byte chunk that belongs in that (swizzled) granule.  The scale bytes are
 // few; they pass through registers and are scattered into their operand
-// order with byte stores (scale_store).
+// order with small stores (scale_store).
 // LDS-destination copy of one 16-byte chunk per lane (device code only: the
 // builtin takes an LDS address-space pointer, which the host pass cannot form)
 __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_base) {
@@ -107,25 +125,35 @@ __device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_base) {
 #endif
 }
 
+// Per-lane source offsets of the DMA: loop-invariant, computed once.  The
+// wave index is uniform; keeping it scalar makes each LDS base (M0) a scalar
+// value, and 32-bit lane offsets let the loads use a scalar 64-bit base.
 template <int D>
-__device__ __forceinline__ void codes_dma(const Params& p, int64_t bh, int kt, uint8_t* stage, int tid) {
+struct DmaPlan {
+  static constexpr int KU = kBc * D / 2 / 16 / 256;  // K^ granules per lane
+  static constexpr int VU = 64 * D / 16 / 256;       // V^ granules per lane
+  uint32_t koff[KU];
+  int lds0;  // 16 * (64 * wave): granule base of this wave in each 256-granule round
+  __device__ __forceinline__ DmaPlan(int tid) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    lds0 = 16 * 64 * wave;
+#pragma unroll
+    for (int u = 0; u < KU; ++u) koff[u] = (uint32_t)(16 * kc_source_chunk<D>(u * 256 + wave * 64 + lane));
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void codes_dma(const Params& p, const DmaPlan<D>& plan, int64_t bh, int kt, uint8_t* stage,
+                                          int tid) {
   using L = Lds<D>;
-  constexpr int KG = kBc * D / 2 / 16;  // K^ granules per tile
-  constexpr int VG = 64 * D / 16;       // V^ granules per tile
   const int NBp = p.Np / 32;
-  const int wave = tid >> 6, lane = tid & 63;
+  const uint32_t voff = (uint32_t)(plan.lds0 + 16 * (tid & 63));
   const uint8_t* kb = p.kc + (bh * p.Np + (int64_t)kt * kBc) * (D / 2);
   const uint8_t* vb = p.vc + (bh * NBp + (int64_t)kt * 4) * D * 16;
 #pragma unroll
-  for (int u = 0; u < KG / 256; ++u) {
-    const int G0 = u * 256 + wave * 64;
-    dma16(kb + 16 * kc_source_chunk<D>(G0 + lane), stage + L::KC + 16 * G0);
-  }
+  for (int u = 0; u < DmaPlan<D>::KU; ++u) dma16(kb + plan.koff[u], stage + L::KC + u * 4096 + plan.lds0);
 #pragma unroll
-  for (int u = 0; u < VG / 256; ++u) {
-    const int G0 = u * 256 + wave * 64;
-    dma16(vb + 16 * (G0 + lane), stage + L::VC + 16 * G0);
-  }
+  for (int u = 0; u < DmaPlan<D>::VU; ++u) dma16(vb + u * 4096 + voff, stage + L::VC + u * 4096 + plan.lds0);
 }
 
 struct ScaleRegs {
@@ -133,6 +161,8 @@ struct ScaleRegs {
   uint32_t vs;
 };
 
+// thread k < 128 loads the d/32 scale bytes of key k; thread j < d loads
+// scale bytes 4j..4j+3 of the tile's [block][channel] V^ scales
 template <int D>
 __device__ __forceinline__ ScaleRegs scale_load(const Params& p, int64_t bh, int kt, int tid) {
   const int NBp = p.Np / 32;
@@ -146,21 +176,35 @@ __device__ __forceinline__ ScaleRegs scale_load(const Params& p, int64_t bh, int
   return r;
 }
 
+// Scatter the scale bytes into per-lane operand order.
+//   K^: lane r + 32g, dword t/2, byte (t%2)(d/64) + h holds the scale of key
+//       tile_key(t, r), d-block 2h + g (the A operand of S^T sub-tile t, step h);
+//   V^: lane L, dword h, byte ct holds the scale of block 2h + L/32, channel
+//       32ct + L%32 (the A operand of PV step h, channel tile ct).
 template <int D>
-__device__ __forceinline__ void scale_store(const ScaleRegs& r, uint8_t* stage, int tid) {
+__device__ __forceinline__ void scale_store(const ScaleRegs& sr, uint8_t* stage, int tid) {
   using L = Lds<D>;
   if (tid < kBc) {
-    const int k = tid, g = k >> 5, t = (k >> 2) & 7, i = k & 3, rr = 4 * g + i;
-#pragma unroll
-    for (int c = 0; c < D / 32; ++c) stage[L::KS + (c * 16 + rr) * 8 + t] = (uint8_t)(r.ks >> (8 * c));
+    const int k = tid;
+    const int t = 2 * (k >> 6) + ((k >> 4) & 1);
+    const int r = 8 * ((k >> 2) & 3) + 4 * ((k >> 5) & 1) + (k & 3);
+    uint8_t* base = stage + L::KS + 4 * (t >> 1);
+    const uint32_t s = sr.ks;
+    if constexpr (D == 128) {
+      *reinterpret_cast<uint16_t*>(base + 8 * r + 2 * (t & 1)) = (uint16_t)((s & 0xFFu) | ((s >> 8) & 0xFF00u));
+      *reinterpret_cast<uint16_t*>(base + 8 * (r + 32) + 2 * (t & 1)) =
+          (uint16_t)(((s >> 8) & 0xFFu) | ((s >> 16) & 0xFF00u));
+    } else {
+      base[8 * r + (t & 1)] = (uint8_t)(s & 0xFFu);
+      base[8 * (r + 32) + (t & 1)] = (uint8_t)((s >> 8) & 0xFFu);
+    }
   }
   if (tid < D) {
-    const int g = (4 * tid) / D;
+    const int bl = (4 * tid) / D, ch0 = (4 * tid) % D;
+    const int lane0 = 32 * (bl & 1) + (ch0 & 31);
+    uint8_t* base = stage + L::VS + 4 * (bl >> 1) + (ch0 >> 5);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int ch = (4 * tid) % D + j, ct = ch / 16, rr = ch % 16;
-      stage[L::VS + (g * 16 + rr) * (D / 16) + ct] = (uint8_t)(r.vs >> (8 * j));
-    }
+    for (int j = 0; j < 4; ++j) base[8 * (lane0 + j)] = (uint8_t)(sr.vs >> (8 * j));
   }
 }
 
@@ -169,28 +213,63 @@ __device__ __forceinline__ v8i as_op(uint4 a) {
   return r;
 }
 
-template <int OPSEL_A>
-__device__ __forceinline__ v4f mfma4(uint4 a, uint4 b, v4f c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as_op(a), as_op(b), c, 4, 4, OPSEL_A, sa, 0, sb);
+template <int OA, int OB>
+__device__ __forceinline__ v16f mfma32(uint4 a, uint4 b, v16f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(as_op(a), as_op(b), c, 4, 4, OA, sa, OB, sb);
+}
+
+// scale-byte selectors are immediates; after unrolling oa and ob are constants
+__device__ __forceinline__ v16f mfma32_sel(int oa, int ob, uint4 a, uint4 b, v16f c, int sa, int sb) {
+  if (ob == 0) {
+    switch (oa) {
+      case 0: return mfma32<0, 0>(a, b, c, sa, sb);
+      case 1: return mfma32<1, 0>(a, b, c, sa, sb);
+      case 2: return mfma32<2, 0>(a, b, c, sa, sb);
+      default: return mfma32<3, 0>(a, b, c, sa, sb);
+    }
+  }
+  switch (oa) {
+    case 0: return mfma32<0, 1>(a, b, c, sa, sb);
+    case 1: return mfma32<1, 1>(a, b, c, sa, sb);
+    case 2: return mfma32<2, 1>(a, b, c, sa, sb);
+    default: return mfma32<3, 1>(a, b, c, sa, sb);
+  }
+}
+
+__device__ __forceinline__ v4f mfma16(uint4 a, uint4 b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as_op(a), as_op(b), c, 4, 4, 0, sa, 0, sb);
 }
 
 // Shared-scale exponent of a block with max M >= 0 from the binary32 fields
-// of M (see the quantizer kernels for the derivation).
+// of M (see the quantizer kernels for the derivation); M = 0 gives 0, a
+// subnormal M the clamp value -127.  Written without branches: M comes from
+// exp2 and is never negative, infinite or NaN.
 template <int RULE>
 __device__ __forceinline__ int scale_exponent(float M) {
   const uint32_t b = __float_as_uint(M);
-  if (b == 0u) return 0;
   const int E = (int)(b >> 23);
-  if (E == 0) return -127;
   int e = E - 129;
   if constexpr (RULE == kRuleUos) e += ((b & 0x7FFFFFu) > 0x680000u) ? 1 : 0;
-  return e < -127 ? -127 : (e > 127 ? 127 : e);
+  e = e < -127 ? -127 : (e > 127 ? 127 : e);
+  return b == 0u ? 0 : e;
 }
 
-__device__ __forceinline__ float xor_lanes(float v, int m) { return __shfl_xor(v, m, 64); }
+// max / sum over the two lanes L and L^32 that hold the same query; both
+// lanes get the same value (the sum is formed in the same order in both)
+__device__ __forceinline__ float pair_max(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(x[0]), __uint_as_float(x[1]));
+}
+__device__ __forceinline__ float pair_sum(float v) {
+  const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(x[0]) + __uint_as_float(x[1]);
+}
 
+// eight E2M1 codes, element 2k in the low nibble of byte k; the four converts
+// write all four bytes, so the merge input of the first one is irrelevant
+// (passing y[0]'s bits spares a register clear)
 __device__ __forceinline__ uint32_t pack_fp4x8(const float* y) {
-  uint32_t w = 0;
+  uint32_t w = __float_as_uint(y[0]);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], 1.0f, 0);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], 1.0f, 1);
   w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], 1.0f, 2);
@@ -198,8 +277,7 @@ __device__ __forceinline__ uint32_t pack_fp4x8(const float* y) {
   return w;
 }
 
-// Per-query state of one 16-query sub-block, replicated in the four lanes that
-// share a query.
+// Per-query state, replicated in the two lanes that share a query.
 struct RowState {
   float m;    // running max of raw scores (or m* for POSTNORM)
   float mc;   // m * c + off
@@ -209,7 +287,6 @@ struct RowState {
 
 template <int D, int MODE, int RULE>
 struct FwdConsts {
-  static constexpr int NCT = D / 16;  // 16-channel output tiles
   // Exponent arguments.  The fused path evaluates (s - m) c as one
   // fma(s, c, -m c); the row maximum then gives P~ = 1 within an ulp, which
   // the UOS rule maps to the interior value 4.  The OCP rule puts P~ = 1 on
@@ -221,184 +298,153 @@ struct FwdConsts {
   static constexpr float kInvSqrtD = (D == 128) ? 0x1.6a09e6p-4f : 0x1p-3f;  // 1/sqrt(d)
 };
 
-// Online-softmax update and P^ of one 16-query sub-block for one key tile:
-// s holds the lane's 32 scores (one 32-key block of query L%16).  Returns the
-// packed FP4 B operand of the PV product; writes its E8M0 scale and alpha.
+// P^ of one 32-key block of the lane's query: the 16 scores of sub-tile pair
+// (s0, s1) in key order, block max bmax.  Returns the packed FP4 B operand of
+// the PV step; writes its E8M0 scale and (DIRECT) the block's contribution to
+// the unquantized row sum.
 template <int D, int MODE, int RULE>
-__device__ __forceinline__ uint4 softmax_block(v4f (&s)[8], RowState& rs, int& psc, float& alpha) {
+__device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, float bmax, const RowState& rs,
+                                                int& psc, float& lpart) {
   using F = FwdConsts<D, MODE, RULE>;
-  float bmax = s[0][0];
+  // block scale from the block max of the exponentials (exp is monotone)
+  const float Mb = F::kExactArg ? __builtin_amdgcn_exp2f(fmaf(bmax - rs.m, F::kC, -rs.off))
+                                : __builtin_amdgcn_exp2f(fmaf(bmax, F::kC, -rs.mc));
+  const int e = scale_exponent<RULE>(Mb);
+  float y[32];
+  if constexpr (F::kExactArg) {
+    const float nb = -(rs.off + (float)e);
 #pragma unroll
-  for (int t = 0; t < 8; ++t)
+    for (int k = 0; k < 16; ++k) {
+      y[k] = __builtin_amdgcn_exp2f(fmaf(s0[k] - rs.m, F::kC, nb));
+      y[16 + k] = __builtin_amdgcn_exp2f(fmaf(s1[k] - rs.m, F::kC, nb));
+    }
+  } else {
+    const float nb = -(rs.mc + (float)e);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bmax = fmaxf(bmax, s[t][i]);
+    for (int k = 0; k < 16; ++k) {
+      y[k] = __builtin_amdgcn_exp2f(fmaf(s0[k], F::kC, nb));
+      y[16 + k] = __builtin_amdgcn_exp2f(fmaf(s1[k], F::kC, nb));
+    }
+  }
+  if constexpr (MODE == kModeDirect) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) sum += y[k];
+    lpart = __builtin_amdgcn_ldexpf(sum, e);
+  }
+  psc = e + 127;
+  return make_uint4(pack_fp4x8(y), pack_fp4x8(y + 8), pack_fp4x8(y + 16), pack_fp4x8(y + 24));
+}
+
+// scores of keys the query may not see -> -inf (element 4j+i of sub-tile t
+// of lane group g is key 64(t/2) + 32g + 16(t%2) + 4j + i of the tile)
+template <bool CAUSAL, bool MASKED>
+__device__ __forceinline__ void mask_scores(v16f (&s)[4], int kt, int N, int q, int g) {
+  if constexpr (MASKED) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = kt * kBc + 64 * (t >> 1) + 32 * g + 16 * (t & 1) + e;
+        if (!(key < N && (!CAUSAL || key <= q))) s[t][e] = -INFINITY;
+      }
+  }
+}
+
+// one running chain, which the compiler turns into v_max3_f32 (two new
+// elements per instruction)
+__device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
+  float m = a[0];
+#pragma unroll
+  for (int k = 1; k < 16; ++k) m = fmaxf(m, a[k]);
+#pragma unroll
+  for (int k = 0; k < 16; ++k) m = fmaxf(m, b[k]);
+  return m;
+}
+
+// One key tile for the wave's 32 queries.  Order: all S products; block and
+// row maxima; P^ of the first 64-key half and its PV products, which run on
+// the matrix cores while P^ of the second half is formed; then the second
+// half's PV products.  MASKED tiles (the ragged last tile and the causal
+// diagonal) set scores of invisible keys to -inf; every other tile runs
+// without any per-element test.
+template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
+__device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[D / 64],
+                                          int qsc, int q, uint4 ones, RowState& rs, v16f (&acc)[D / 32], v4f& accl,
+                                          int lane) {
+  using L = Lds<D>;
+  using F = FwdConsts<D, MODE, RULE>;
+  constexpr int NH = D / 64;   // K steps of one S^T sub-tile
+  constexpr int NCT = D / 32;  // 32-channel output tiles
+  const int r = lane & 31, g = lane >> 5;
+
+  // ---- S^T = K^ Q^T for 128 keys x 32 queries
+  const uint2 ksw = *reinterpret_cast<const uint2*>(buf + L::KS + 8 * lane);
+  uint4 kop[4][NH];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      kop[t][h] = *reinterpret_cast<const uint4*>(buf + L::KC + 16 * kc_granule<D>(tile_key(t, r), 2 * h + g));
+  v16f s[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    s[t] = v16f{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+      s[t] = mfma32_sel((t & 1) * NH + h, h, kop[t][h], qop[h], s[t], (t < 2) ? (int)ksw.x : (int)ksw.y, qsc);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- running max, block maxima, alpha
+  mask_scores<CAUSAL, MASKED>(s, kt, N, q, g);
+  float bmax[2];
+  bmax[0] = max32(s[0], s[1]);
+  bmax[1] = max32(s[2], s[3]);
   float a = 1.0f;
   if constexpr (MODE != kModePostnorm) {
-    float rmax = fmaxf(bmax, xor_lanes(bmax, 16));
-    rmax = fmaxf(rmax, xor_lanes(rmax, 32));
-    const float m_new = fmaxf(rs.m, rmax);
+    const float m_new = fmaxf(rs.m, pair_max(fmaxf(bmax[0], bmax[1])));
     if (m_new != -INFINITY) {
       a = __builtin_amdgcn_exp2f((rs.m - m_new) * F::kC);  // 0 on the first visited tile
       rs.m = m_new;
       rs.mc = m_new * F::kC;
     }
   }
-  alpha = a;
-  const float mc = rs.mc, mref = rs.m, off = rs.off;
   if constexpr (MODE == kModeStats) {
     float sum = 0.0f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sum += __builtin_amdgcn_exp2f((s[t][i] - mref) * F::kC);
-    sum += xor_lanes(sum, 16);
-    sum += xor_lanes(sum, 32);
-    rs.l = a * rs.l + sum;
-    psc = 127;
-    return make_uint4(0, 0, 0, 0);
+      for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f((s[t][e] - rs.m) * F::kC);
+    rs.l = a * rs.l + pair_sum(sum);
   } else {
-    // block scale from the block max of the exponentials (exp is monotone)
-    const float Mb = F::kExactArg ? __builtin_amdgcn_exp2f(fmaf(bmax - mref, F::kC, -off))
-                                  : __builtin_amdgcn_exp2f(fmaf(bmax, F::kC, -mc));
-    const int e = scale_exponent<RULE>(Mb);
-    float y[32];
-    if constexpr (F::kExactArg) {
-      const float nb = -(off + (float)e);
+    const uint2 vsw = *reinterpret_cast<const uint2*>(buf + L::VS + 8 * lane);
+    if constexpr (MODE != kModePostnorm) {
+      if (__any(a != 1.0f)) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[t][i] - mref, F::kC, nb));
-    } else {
-      const float nb = -(mc + (float)e);
-#pragma unroll
-      for (int t = 0; t < 8; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) y[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(s[t][i], F::kC, nb));
-    }
-    if constexpr (MODE == kModeDirect) {
-      float sum = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 32; ++k) sum += y[k];
-      sum = __builtin_amdgcn_ldexpf(sum, e);
-      sum += xor_lanes(sum, 16);
-      sum += xor_lanes(sum, 32);
-      rs.l = a * rs.l + sum;
-    }
-    psc = e + 127;
-    return make_uint4(pack_fp4x8(y), pack_fp4x8(y + 8), pack_fp4x8(y + 16), pack_fp4x8(y + 24));
-  }
-}
-
-template <int D, bool CAUSAL, bool MASKED>
-__device__ __forceinline__ void mask_scores(v4f (&s)[8], int kt, int N, int q, int grp) {
-  if constexpr (MASKED) {
-#pragma unroll
-    for (int t = 0; t < 8; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kt * kBc + 32 * grp + 4 * t + i;
-        if (!(key < N && (!CAUSAL || key <= q))) s[t][i] = -INFINITY;
-      }
-  }
-}
-
-// O~ (and the l column) of one sub-block: rescale by alpha when a running
-// max moved, then accumulate P^ V^ and P^ 1 with the matrix cores.
-template <int D, int MODE>
-__device__ __forceinline__ void pv_block(const uint4 (&vop)[D / 16], uint2 vsw, uint4 pq, int psc, float alpha,
-                                         v4f (&acc)[D / 16 + 1]) {
-  constexpr int NCT = D / 16;
-  if constexpr (MODE != kModePostnorm) {
-    if (__any(alpha != 1.0f)) {
-#pragma unroll
-      for (int ct = 0; ct <= NCT; ++ct) acc[ct] *= alpha;
-    }
-  }
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const int sc = (ct < 4) ? (int)vsw.x : (int)vsw.y;
-    switch (ct & 3) {
-      case 0: acc[ct] = mfma4<0>(vop[ct], pq, acc[ct], sc, psc); break;
-      case 1: acc[ct] = mfma4<1>(vop[ct], pq, acc[ct], sc, psc); break;
-      case 2: acc[ct] = mfma4<2>(vop[ct], pq, acc[ct], sc, psc); break;
-      default: acc[ct] = mfma4<3>(vop[ct], pq, acc[ct], sc, psc); break;
-    }
-  }
-  const uint4 ones = make_uint4(0x22222222u, 0x22222222u, 0x22222222u, 0x22222222u);  // E2M1 1.0
-  acc[NCT] = mfma4<0>(ones, pq, acc[NCT], 127, psc);
-}
-
-// One key tile for the wave's 32 queries, ordered so the matrix cores and the
-// vector ALU overlap inside the wave: both sub-blocks' S products are issued
-// first; the softmax of sub-block 0 runs while those of sub-block 1 are in
-// flight; its PV products are issued before the softmax of sub-block 1, which
-// then runs while they execute.  MASKED tiles (the ragged last tile and the
-// causal diagonal) set scores of invisible keys to -inf; every other tile runs
-// without any per-element test.
-template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
-__device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[2],
-                                          const int (&qsc)[2], const int (&qi)[2], RowState (&rs)[2],
-                                          v4f (&acc)[2][D / 16 + 1], int r16, int grp) {
-  using L = Lds<D>;
-  constexpr int NCT = D / 16;
-  // ---- S^T = K^ Q^T for 128 keys x 32 queries
-  uint2 ksw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-  if (grp < D / 32) ksw = *reinterpret_cast<const uint2*>(buf + L::KS + (grp * 16 + r16) * 8);
-  uint4 kop[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    const int k = 32 * (r16 >> 2) + 4 * t + (r16 & 3);
-    kop[t] = *reinterpret_cast<const uint4*>(buf + L::KC + 16 * kc_granule<D>(k, grp & (D / 32 - 1)));
-    if (D == 64 && grp >= 2) kop[t] = make_uint4(0, 0, 0, 0);
-  }
-  v4f s0[8], s1[8];
-  const v4f z = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    v4f (&s)[8] = sb ? s1 : s0;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int sc = (t < 4) ? (int)ksw.x : (int)ksw.y;
-      switch (t & 3) {
-        case 0: s[t] = mfma4<0>(kop[t], qop[sb], z, sc, qsc[sb]); break;
-        case 1: s[t] = mfma4<1>(kop[t], qop[sb], z, sc, qsc[sb]); break;
-        case 2: s[t] = mfma4<2>(kop[t], qop[sb], z, sc, qsc[sb]); break;
-        default: s[t] = mfma4<3>(kop[t], qop[sb], z, sc, qsc[sb]); break;
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] *= a;
+        accl *= a;
       }
     }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-
-  // ---- sub-block 0: softmax and P^, while the S products of sub-block 1 run
-  mask_scores<D, CAUSAL, MASKED>(s0, kt, N, qi[0], grp);
-  int psc0;
-  float a0;
-  const uint4 pq0 = softmax_block<D, MODE, RULE>(s0, rs[0], psc0, a0);
-  __builtin_amdgcn_sched_barrier(0);
-
-  if constexpr (MODE != kModeStats) {
-    uint2 vsw = make_uint2(0x7F7F7F7Fu, 0x7F7F7F7Fu);
-    if constexpr (D == 128) vsw = *reinterpret_cast<const uint2*>(buf + L::VS + (grp * 16 + r16) * 8);
-    else vsw.x = *reinterpret_cast<const uint32_t*>(buf + L::VS + (grp * 16 + r16) * 4);
-    uint4 vop[NCT];
+    float lsum = 0.0f;
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      vop[ct] = *reinterpret_cast<const uint4*>(buf + L::VC + 16 * (grp * D + 16 * ct + r16));
-    pv_block<D, MODE>(vop, vsw, pq0, psc0, a0, acc[0]);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // ---- sub-block 1, while the PV products of sub-block 0 run
-    mask_scores<D, CAUSAL, MASKED>(s1, kt, N, qi[1], grp);
-    int psc1;
-    float a1;
-    const uint4 pq1 = softmax_block<D, MODE, RULE>(s1, rs[1], psc1, a1);
-    __builtin_amdgcn_sched_barrier(0);
-    pv_block<D, MODE>(vop, vsw, pq1, psc1, a1, acc[1]);
-  } else {
-    mask_scores<D, CAUSAL, MASKED>(s1, kt, N, qi[1], grp);
-    int psc1;
-    float a1;
-    (void)softmax_block<D, MODE, RULE>(s1, rs[1], psc1, a1);
+    for (int hb = 0; hb < 2; ++hb) {
+      uint4 vop[NCT];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        vop[ct] = *reinterpret_cast<const uint4*>(buf + L::VC + 16 * ((2 * hb + g) * D + 32 * ct + r));
+      int psc;
+      float lpart = 0.0f;
+      const uint4 pq = quantize_block<D, MODE, RULE>(s[2 * hb], s[2 * hb + 1], bmax[hb], rs, psc, lpart);
+      lsum += lpart;
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        acc[ct] = mfma32_sel(ct, 0, vop[ct], pq, acc[ct], hb ? (int)vsw.y : (int)vsw.x, psc);
+      accl = mfma16(ones, pq, accl, 127, psc);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (MODE == kModeDirect) rs.l = a * rs.l + pair_sum(lsum);
   }
 }
 
@@ -406,12 +452,13 @@ template <int D, bool CAUSAL, int MODE, int RULE>
 __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   using L = Lds<D>;
   using F = FwdConsts<D, MODE, RULE>;
-  constexpr int NCT = F::NCT;
+  constexpr int NH = D / 64;
+  constexpr int NCT = D / 32;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int r16 = lane & 15, grp = lane >> 4;
+  const int r = lane & 31, g = lane >> 5;
 
   // workgroup -> (head, query tile); consecutive logical tiles land on the
   // same XCD (the hardware deals workgroups round-robin over 8 XCDs) so the
@@ -427,43 +474,40 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   // leading tiles in which every key is visible to every query of the tile
   const int nfull = CAUSAL ? min(qt, nkt) : p.N / kBc;
 
-  // Q^ operands of the two sub-blocks (B operand: lane = query L%16, d-chunk L/16)
-  uint4 qop[2];
-  int qsc[2], qi[2];
+  // Q^ operand (B operand of S^T: lane = query L%32, d-chunk 2h + L/32 in
+  // step h) and its scales (byte h = d-block 2h + L/32)
+  const int qi = qt * kBr + 32 * wave + r;
+  const int64_t qrow = bh * p.Np + qi;
+  uint4 qop[NH];
+  int qsc;
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    qi[sb] = qt * kBr + 32 * wave + 16 * sb + r16;
-    const int64_t row = bh * p.Np + qi[sb];
-    if (grp < D / 32) {
-      qop[sb] = *reinterpret_cast<const uint4*>(p.qc + row * (D / 2) + 16 * grp);
-      qsc[sb] = p.qs[row * (D / 32) + grp];
-    } else {
-      qop[sb] = make_uint4(0, 0, 0, 0);
-      qsc[sb] = 127;
-    }
-  }
+  for (int h = 0; h < NH; ++h) qop[h] = *reinterpret_cast<const uint4*>(p.qc + qrow * (D / 2) + 16 * (2 * h + g));
+  if constexpr (D == 128) qsc = (int)p.qs[qrow * 4 + g] | ((int)p.qs[qrow * 4 + 2 + g] << 8);
+  else qsc = (int)p.qs[qrow * 2 + g];
 
-  RowState rs[2];
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    rs[sb].m = -INFINITY;
-    rs[sb].mc = 0.0f;
-    rs[sb].off = 0.0f;
-    rs[sb].l = 0.0f;
-    if constexpr (MODE == kModePostnorm) {
-      const float* st = p.stats + (bh * p.Np + qi[sb]) * 2;
-      rs[sb].m = st[0];
-      rs[sb].off = __builtin_amdgcn_logf(st[1]);  // log2 of l*
-      rs[sb].mc = st[0] * F::kC + rs[sb].off;
-    }
-  }
-  v4f acc[2][NCT + 1];
-#pragma unroll
-  for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-    for (int ct = 0; ct <= NCT; ++ct) acc[sb][ct] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  // 0/1 A operand of the l product (row L%16, K chunk L/16)
+  const uint32_t onew = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 0x22222222u : 0u;  // E2M1 1.0
+  const uint4 ones = make_uint4(onew, onew, onew, onew);
 
-  codes_dma<D>(p, bh, 0, lds, tid);
+  RowState rs;
+  rs.m = -INFINITY;
+  rs.mc = 0.0f;
+  rs.off = 0.0f;
+  rs.l = 0.0f;
+  if constexpr (MODE == kModePostnorm) {
+    const float* st = p.stats + qrow * 2;
+    rs.m = st[0];
+    rs.off = __builtin_amdgcn_logf(st[1]);  // log2 of l*
+    rs.mc = st[0] * F::kC + rs.off;
+  }
+  v16f acc[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+    acc[ct] = v16f{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+  v4f accl = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+
+  const DmaPlan<D> plan(tid);
+  codes_dma<D>(p, plan, bh, 0, lds, tid);
   scale_store<D>(scale_load<D>(p, bh, 0, tid), lds, tid);
   __builtin_amdgcn_s_waitcnt(0);  // the DMA has landed in LDS
   __syncthreads();
@@ -475,51 +519,50 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
     const uint8_t* buf = lds + (kt & 1) * L::STAGE;
     uint8_t* nxt = lds + ((kt + 1) & 1) * L::STAGE;
     const int kn = min(kt + 1, nkt - 1);
-    codes_dma<D>(p, bh, kn, nxt, tid);
+    codes_dma<D>(p, plan, bh, kn, nxt, tid);
     const ScaleRegs sr = scale_load<D>(p, bh, kn, tid);
-    tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, rs, acc, r16, grp);
+    tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, rs, acc, accl, lane);
     scale_store<D>(sr, nxt, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   // at most one masked tile: the ragged end of the keys or the causal diagonal
   if (nfull < nkt)
-    tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, rs, acc,
-                                           r16, grp);
+    tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, ones, rs, acc,
+                                           accl, lane);
 
   // ---- epilogue
+  if constexpr (MODE == kModeStats) {
+    if (g == 0) {
+      float* st2 = p.stats + qrow * 2;
+      st2[0] = rs.m;
+      st2[1] = rs.l;
+    }
+    return;
+  }
+  if (qi >= p.N) return;
+  const float lsum = accl[0];  // sum of beta-weighted P^ (the 0/1 product)
+  // O = O~ / l with a correctly rounded division (Eq. 8): with V^ constant
+  // per channel, O~ = v^ l exactly, and the division returns v^ exactly
+  float l;
+  if constexpr (MODE == kModePnq) l = lsum;
+  else if constexpr (MODE == kModeDirect) l = rs.l;
+  else l = 1.0f;
+  float* orow = p.out + (bh * p.N + qi) * D + 4 * g;
 #pragma unroll
-  for (int sb = 0; sb < 2; ++sb) {
-    const int q = qi[sb];
-    if constexpr (MODE == kModeStats) {
-      if (grp == 0) {
-        float* st2 = p.stats + (bh * p.Np + q) * 2;
-        st2[0] = rs[sb].m;
-        st2[1] = rs[sb].l;
-      }
-      continue;
-    }
-    if (q >= p.N) continue;
-    const float lsum = acc[sb][NCT][0];  // sum of beta-weighted P^ (the ones column)
-    // O = O~ / l with a correctly rounded division (Eq. 8): with V^ constant
-    // per channel, O~ = v^ l exactly, and the division returns v^ exactly
-    float l;
-    if constexpr (MODE == kModePnq) l = lsum;
-    else if constexpr (MODE == kModeDirect) l = rs[sb].l;
-    else l = 1.0f;
-    float* orow = p.out + (bh * p.N + q) * D + 4 * grp;
+  for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const v4f o = acc[sb][ct];
-      *reinterpret_cast<float4*>(orow + 16 * ct) = make_float4(o[0] / l, o[1] / l, o[2] / l, o[3] / l);
+    for (int j = 0; j < 4; ++j) {
+      const v16f& o = acc[ct];
+      *reinterpret_cast<float4*>(orow + 32 * ct + 8 * j) =
+          make_float4(o[4 * j] / l, o[4 * j + 1] / l, o[4 * j + 2] / l, o[4 * j + 3] / l);
     }
-    if (grp == 0) {
-      if (p.row_stats) {
-        p.row_stats[(bh * p.N + q) * 2 + 0] = rs[sb].m * F::kInvSqrtD;
-        p.row_stats[(bh * p.N + q) * 2 + 1] = l;
-      }
-      if (p.row_sums) p.row_sums[bh * p.N + q] = (MODE == kModePostnorm) ? lsum : lsum / l;
+  if (g == 0) {
+    if (p.row_stats) {
+      p.row_stats[(bh * p.N + qi) * 2 + 0] = rs.m * F::kInvSqrtD;
+      p.row_stats[(bh * p.N + qi) * 2 + 1] = l;
     }
+    if (p.row_sums) p.row_sums[bh * p.N + qi] = (MODE == kModePostnorm) ? lsum : lsum / l;
   }
 }
 
