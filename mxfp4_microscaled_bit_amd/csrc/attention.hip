@@ -240,6 +240,19 @@ __device__ __forceinline__ v4f mfma16(uint4 a, uint4 b, v4f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(as_op(a), as_op(b), c, 4, 4, 0, sa, 0, sb);
 }
 
+// The E8M0 scale operands of the scaled MFMAs are read by the matrix core
+// after the instruction issues (rows of a 32x32 product that execute in later
+// passes see later register contents), but the compiler treats them as read
+// at issue and may reuse their registers at once.  Every scale register is
+// therefore kept live until a value exists that the matrix core can only
+// have produced after that product: keep_live() ties the registers to such a
+// value with an empty asm statement.  The PV products of a tile are followed,
+// on the same matrix core, by the S products of the next tile, so the next
+// tile's score maximum serves; after the last tile, the accumulators do.
+__device__ __forceinline__ void keep_live(float after, int a, int b = 0, int c = 0, int d = 0) {
+  asm volatile("" ::"v"(after), "v"(a), "v"(b), "v"(c), "v"(d));
+}
+
 // Shared-scale exponent of a block with max M >= 0 from the binary32 fields
 // of M (see the quantizer kernels for the derivation); M = 0 gives 0, a
 // subnormal M the clamp value -127.  Written without branches: M comes from
@@ -370,8 +383,8 @@ __device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
 // without any per-element test.
 template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
 __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[D / 64],
-                                          int qsc, int q, uint4 ones, RowState& rs, v16f (&acc)[D / 32], v4f& accl,
-                                          int lane) {
+                                          int qsc, int q, uint4 ones, int one_sc, RowState& rs, v16f (&acc)[D / 32],
+                                          v4f& accl, int (&held)[4], int lane) {
   using L = Lds<D>;
   using F = FwdConsts<D, MODE, RULE>;
   constexpr int NH = D / 64;   // K steps of one S^T sub-tile
@@ -401,9 +414,14 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   float bmax[2];
   bmax[0] = max32(s[0], s[1]);
   bmax[1] = max32(s[2], s[3]);
+  const float tmax = fmaxf(bmax[0], bmax[1]);
+  // this tile's S products and the previous tile's PV products have read
+  // their scales once tmax exists
+  keep_live(tmax, (int)ksw.x, (int)ksw.y, one_sc);
+  keep_live(tmax, held[0], held[1], held[2], held[3]);
   float a = 1.0f;
   if constexpr (MODE != kModePostnorm) {
-    const float m_new = fmaxf(rs.m, pair_max(fmaxf(bmax[0], bmax[1])));
+    const float m_new = fmaxf(rs.m, pair_max(tmax));
     if (m_new != -INFINITY) {
       a = __builtin_amdgcn_exp2f((rs.m - m_new) * F::kC);  // 0 on the first visited tile
       rs.m = m_new;
@@ -441,9 +459,12 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct)
         acc[ct] = mfma32_sel(ct, 0, vop[ct], pq, acc[ct], hb ? (int)vsw.y : (int)vsw.x, psc);
-      accl = mfma16(ones, pq, accl, 127, psc);
+      accl = mfma16(ones, pq, accl, one_sc, psc);
       __builtin_amdgcn_sched_barrier(0);
+      held[2 + hb] = psc;
     }
+    held[0] = (int)vsw.x;
+    held[1] = (int)vsw.y;
     if constexpr (MODE == kModeDirect) rs.l = a * rs.l + pair_sum(lsum);
   }
 }
@@ -488,6 +509,9 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   // 0/1 A operand of the l product (row L%16, K chunk L/16)
   const uint32_t onew = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 0x22222222u : 0u;  // E2M1 1.0
   const uint4 ones = make_uint4(onew, onew, onew, onew);
+  int one_sc = 127;                 // E8M0 x1, in a register of its own
+  asm volatile("" : "+v"(one_sc));  // (never rematerialized; see keep_live)
+  int held[4] = {0, 0, 0, 0};       // scale registers of the latest PV products
 
   RowState rs;
   rs.m = -INFINITY;
@@ -521,15 +545,15 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
     const int kn = min(kt + 1, nkt - 1);
     codes_dma<D>(p, plan, bh, kn, nxt, tid);
     const ScaleRegs sr = scale_load<D>(p, bh, kn, tid);
-    tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, rs, acc, accl, lane);
+    tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, one_sc, rs, acc, accl, held, lane);
     scale_store<D>(sr, nxt, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
   // at most one masked tile: the ragged end of the keys or the causal diagonal
   if (nfull < nkt)
-    tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, ones, rs, acc,
-                                           accl, lane);
+    tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, ones, one_sc, rs,
+                                           acc, accl, held, lane);
 
   // ---- epilogue
   if constexpr (MODE == kModeStats) {
@@ -540,8 +564,15 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
     }
     return;
   }
-  if (qi >= p.N) return;
   const float lsum = accl[0];  // sum of beta-weighted P^ (the 0/1 product)
+  {
+    float done = lsum;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) done += acc[ct][0];
+    keep_live(done, held[0], held[1], held[2], held[3]);
+    keep_live(done, one_sc);
+  }
+  if (qi >= p.N) return;
   // O = O~ / l with a correctly rounded division (Eq. 8): with V^ constant
   // per channel, O~ = v^ l exactly, and the division returns v^ exactly
   float l;
