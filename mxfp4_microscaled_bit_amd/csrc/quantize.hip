@@ -71,33 +71,32 @@ __device__ __forceinline__ int scale_exponent(float M) {
 // 2^k as a binary32 for k in [-126, 127].
 __device__ __forceinline__ float pow2f(int k) { return __uint_as_float((uint32_t)(k + 127) << 23); }
 
-// E2M1 code of y: magnitude rounded to nearest, ties to even, saturating at
-// 6; bit 3 is the sign of y (also for results that round to zero).
-//   |y| < 1: the grid step is 0.5, so the code is rint(2|y|) in {0, 1, 2};
-//   |y| >= 1: round the binary32 fraction to one bit (ties to even); the
-//             code of 2^E * 1.m is 2E + 2 + m, capped at 7 (value 6).
-__device__ __forceinline__ uint32_t e2m1_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 28) & 8u;
-  const uint32_t ua = u & 0x7FFFFFFFu;
-  const float a = __uint_as_float(ua);
-  const uint32_t small = (uint32_t)__builtin_rintf(a * 2.0f);
-  const uint32_t r = ua + 0x1FFFFFu + ((ua >> 22) & 1u);
-  const uint32_t big = min((r >> 22) - (127u << 1) + 2u, 7u);
-  return (a < 1.0f ? small : big) | sign;
+// Eight E2M1 codes of y[0..7] / 2^e in one word, element 2k in the low
+// nibble of byte k.  The hardware convert divides by the binary32 scale 2^e
+// (exact for a power of two), rounds to the nearest E2M1 value with ties to
+// the even code, saturates at 6 and keeps the sign of values that round to
+// zero.  The first convert's merge input is irrelevant: the four converts
+// write all four bytes.
+__device__ __forceinline__ uint32_t cvt8(const float* y, float scale) {
+  uint32_t w = __float_as_uint(y[0]);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[0], y[1], scale, 0);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[2], y[3], scale, 1);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[4], y[5], scale, 2);
+  w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, y[6], y[7], scale, 3);
+  return w;
 }
 
-// Packs 32 codes (element 2k in the low nibble of byte k).
-__device__ __forceinline__ uint4 pack32(const uint32_t* c) {
-  uint32_t w[4];
+// Codes of a 32-element block y[] with shared exponent e, 16 bytes.  The scale
+// 2^e is a normal binary32 for e >= -126; at the clamp e = -127 every element
+// is below 2^-124, and ldexp by 127 moves it up exactly before a unit-scale
+// convert.
+__device__ __forceinline__ uint4 block_codes(float* y, int e) {
+  float sc = pow2f(e < -126 ? 0 : e);
+  if (e < -126) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    uint32_t acc = 0;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc |= c[8 * q + j] << (4 * j);
-    w[q] = acc;
+    for (int i = 0; i < 32; ++i) y[i] = __builtin_amdgcn_ldexpf(y[i], 127);
   }
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(cvt8(y, sc), cvt8(y + 8, sc), cvt8(y + 16, sc), cvt8(y + 24, sc));
 }
 
 // One lane owns one 32-channel block of one row (d/32 lanes per row, in the
@@ -185,25 +184,14 @@ __global__ __launch_bounds__(256) void k_quantize_headdim(
     const float M = ROTATE ? mraw * kRotScale : mraw;
     const int e = scale_exponent<RULE>(M);
 
-    uint32_t c[32];
+    // y_i = fl(v_i r), then the exact division by 2^e inside the convert
     if constexpr (ROTATE) {
-      // y_i = fl(v_i r) 2^-e.  When neither fl(v_i r) nor r 2^-e can be
-      // subnormal for an element that quantizes to a nonzero code, this is
-      // fl(v_i (r 2^-e)), a single multiply.
-      if (e >= -120 && e <= 120) {
-        const float s = kRotScale * pow2f(-e);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) c[i] = e2m1_code(v[i] * s);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) c[i] = e2m1_code(__builtin_amdgcn_ldexpf(v[i] * kRotScale, -e));
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) c[i] = e2m1_code(__builtin_amdgcn_ldexpf(v[i], -e));
+      for (int i = 0; i < 32; ++i) v[i] *= kRotScale;
     }
+    const uint4 packed = block_codes(v, e);
     if (unit[it] < total_units) {
-      reinterpret_cast<uint4*>(codes)[unit[it]] = pack32(c);
+      reinterpret_cast<uint4*>(codes)[unit[it]] = packed;
       scales[unit[it]] = (uint8_t)(e + 127);
     }
   }
@@ -242,16 +230,9 @@ __global__ __launch_bounds__(256) void k_quantize_tokens(
     m1 = fmaxf(m1, fabsf(v1[t]));
   }
   const int e0 = scale_exponent<RULE>(m0), e1 = scale_exponent<RULE>(m1);
-  const float s0 = pow2f(-e0), s1 = pow2f(-e1);  // e in [-127, 126]: normal
-  uint32_t c0[32], c1[32];
-#pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    c0[t] = e2m1_code(v0[t] * s0);
-    c1[t] = e2m1_code(v1[t] * s1);
-  }
   uint4* dst = reinterpret_cast<uint4*>(codes + (gblk * D + 2 * cp) * 16);
-  dst[0] = pack32(c0);
-  dst[1] = pack32(c1);
+  dst[0] = block_codes(v0, e0);
+  dst[1] = block_codes(v1, e1);
   *reinterpret_cast<uint16_t*>(scales + gblk * D + 2 * cp) =
       (uint16_t)((uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8));
 }
