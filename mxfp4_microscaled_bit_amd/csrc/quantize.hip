@@ -213,16 +213,29 @@ __global__ __launch_bounds__(256) void k_quantize_tokens(
   const int64_t bh = gblk / NBp;
   const int kb = (int)(gblk % NBp);
   const int64_t b = bh / H, h = bh % H;
-  const uint16_t* base = x + b * sB + h * sH + 2 * cp;
+  const uint16_t* base = x + b * sB + h * sH + (int64_t)(32 * kb) * sN + 2 * cp;
 
+  // all 32 loads are issued before any is used; only a block that crosses N
+  // (the last one) takes the guarded path, decided once per wave
+  uint32_t w[32];
+  if (__all(32 * kb + 31 < N)) {
+    const uint16_t* pt = base;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      w[t] = *reinterpret_cast<const uint32_t*>(pt);
+      pt += sN;
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int tc = min(t, max(N - 1 - 32 * kb, 0));  // an in-range row to read from
+      const uint32_t wt = *reinterpret_cast<const uint32_t*>(base + (int64_t)tc * sN);
+      w[t] = (32 * kb + t < N) ? wt : 0u;
+    }
+  }
   float v0[32], v1[32];
 #pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    const int n = 32 * kb + t;
-    uint32_t w = 0;
-    if (n < N) w = *reinterpret_cast<const uint32_t*>(base + (int64_t)n * sN);
-    unpack2<DTYPE>(w, v0[t], v1[t]);
-  }
+  for (int t = 0; t < 32; ++t) unpack2<DTYPE>(w[t], v0[t], v1[t]);
   float m0 = 0.0f, m1 = 0.0f;
 #pragma unroll
   for (int t = 0; t < 32; ++t) {
