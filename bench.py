@@ -128,14 +128,23 @@ def main():
         sys.exit(1)
 
     if args.copy_probe:
+        # plain device-to-device copies: the reference kernel for scaling the
+        # HBM byte counters, and the achievable read+write bandwidth
         n = args.copy_probe // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
+        times = []
         for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
             dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3}), flush=True)
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        best = min(times)
+        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": 3, "best_ms": round(best, 4),
+                          "read_plus_write_gb_per_s": round(2 * n * 4 / (best * 1e-3) / 1e9, 1)}), flush=True)
         return
 
     w = W.WORKLOADS[args.workload]
