@@ -320,9 +320,19 @@ __device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, 
                                                 int& psc, float& lpart) {
   using F = FwdConsts<D, MODE, RULE>;
   // block scale from the block max of the exponentials (exp is monotone)
-  const float Mb = F::kExactArg ? __builtin_amdgcn_exp2f(fmaf(bmax - rs.m, F::kC, -rs.off))
-                                : __builtin_amdgcn_exp2f(fmaf(bmax, F::kC, -rs.mc));
-  const int e = scale_exponent<RULE>(Mb);
+  int e;
+  if constexpr (F::kExactArg) {
+    e = scale_exponent<RULE>(__builtin_amdgcn_exp2f(fmaf(bmax - rs.m, F::kC, -rs.off)));
+  } else {
+    // UOS in the log domain: e = ceil(log2(Mb) - log2(7.25)) with
+    // log2(Mb) = bmax c - m c, the same argument the exponentials use; its
+    // binary32 rounding moves a scale decision only within the decision
+    // margin of the exp2 evaluation.  A fully masked block (-inf) takes the
+    // clamp; its elements are all zero whatever the scale.
+    const float t = fmaf(bmax, F::kC, -rs.mc) - 0x1.6dd252p+1f;  // log2(7.25)
+    e = (int)__builtin_ceilf(fmaxf(t, -127.0f));
+    e = e > 127 ? 127 : e;
+  }
   float y[32];
   if constexpr (F::kExactArg) {
     const float nb = -(rs.off + (float)e);
@@ -384,7 +394,7 @@ __device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
 template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
 __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[D / 64],
                                           int qsc, int q, uint4 ones, int one_sc, RowState& rs, v16f (&acc)[D / 32],
-                                          v4f& accl, int (&held)[4], int lane) {
+                                          v4f& accl, int (&held)[4], int lane, const int (&koff)[D / 64]) {
   using L = Lds<D>;
   using F = FwdConsts<D, MODE, RULE>;
   constexpr int NH = D / 64;   // K steps of one S^T sub-tile
@@ -398,7 +408,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int h = 0; h < NH; ++h)
-      kop[t][h] = *reinterpret_cast<const uint4*>(buf + L::KC + 16 * kc_granule<D>(tile_key(t, r), 2 * h + g));
+      kop[t][h] = *reinterpret_cast<const uint4*>(buf + koff[h] + (D / 2) * (64 * (t >> 1) + 16 * (t & 1)));
   v16f s[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -512,6 +522,12 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   int one_sc = 127;                 // E8M0 x1, in a register of its own
   asm volatile("" : "+v"(one_sc));  // (never rematerialized; see keep_live)
   int held[4] = {0, 0, 0, 0};       // scale registers of the latest PV products
+  // K^ operand offset of sub-tile 0, step h; sub-tile t adds a constant,
+  // (d/2)(64(t/2) + 16(t%2)) bytes: its key bits 4 and 6 leave the swizzle
+  // term unchanged
+  int koff[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) koff[h] = L::KC + 16 * kc_granule<D>(tile_key(0, r), 2 * h + g);
 
   RowState rs;
   rs.m = -INFINITY;
@@ -545,7 +561,8 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
     const int kn = min(kt + 1, nkt - 1);
     codes_dma<D>(p, plan, bh, kn, nxt, tid);
     const ScaleRegs sr = scale_load<D>(p, bh, kn, tid);
-    tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, one_sc, rs, acc, accl, held, lane);
+    tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, one_sc, rs, acc, accl, held, lane,
+                                            koff);
     scale_store<D>(sr, nxt, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -553,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   // at most one masked tile: the ragged end of the keys or the causal diagonal
   if (nfull < nkt)
     tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, ones, one_sc, rs,
-                                           acc, accl, held, lane);
+                                           acc, accl, held, lane, koff);
 
   // ---- epilogue
   if constexpr (MODE == kModeStats) {
