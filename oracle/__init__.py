@@ -74,7 +74,7 @@ class AttnCfg(ctypes.Structure):
                 ("rotate", ctypes.c_int32), ("quant", ctypes.c_int32), ("rule", ctypes.c_int32),
                 ("p_mode", ctypes.c_int32), ("kv_tile", ctypes.c_int32),
                 ("nthreads", ctypes.c_int32), ("q", ctypes.c_double),
-                ("amb_delta", ctypes.c_double)]
+                ("amb_delta", ctypes.c_double), ("Nk", ctypes.c_int32)]
 
 
 def default_threads() -> int:
@@ -193,8 +193,9 @@ def quantize_token_blocks(x_bits, dtype, B, H, N, d, *, rule=RULE_UOS, q=0.0, bl
 
 def attention(q_bits, k_bits, v_bits, dtype, B, H, N, d, *, causal=False, rotate=True,
               quant=True, rule=RULE_UOS, p_mode=P_PNQ, kv_tile=128, rows=None, strides=None,
-              q=0.0, amb_delta=0.0, nthreads=None):
-    """Attention forward for the listed query rows of every head.
+              q=0.0, amb_delta=0.0, nthreads=None, Nk=None):
+    """Attention forward for the listed query rows of every head.  ``Nk`` is
+    the number of key/value tokens (cross-attention; default N).
 
     Returns a dict with ``out`` [B,H,R,d], ``m``, ``l``, ``rowsum`` [B,H,R], ``amb``
     and ``absmass`` [B,H,R,d] (all float64), R = len(rows) or N.
@@ -204,7 +205,8 @@ def attention(q_bits, k_bits, v_bits, dtype, B, H, N, d, *, causal=False, rotate
     rows_a = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
     R = N if rows_a is None else rows_a.size
     cfg = AttnCfg(B, H, N, d, dtype, int(bool(causal)), int(bool(rotate)), int(bool(quant)), rule,
-                  p_mode, kv_tile, nthreads or default_threads(), float(q), float(amb_delta))
+                  p_mode, kv_tile, nthreads or default_threads(), float(q), float(amb_delta),
+                  0 if Nk is None else int(Nk))
     out = np.empty((B, H, R, d), np.float64)
     m = np.empty((B, H, R), np.float64)
     l = np.empty((B, H, R), np.float64)

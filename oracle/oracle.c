@@ -313,7 +313,9 @@ int oracle_quantize_token_blocks(const uint16_t* x, int dtype, int B, int H, int
 typedef struct {
   const oracle_attn_cfg* cfg;
   const uint16_t *q, *k, *v;
-  int64_t sB, sH, sN;
+  int64_t sB, sH, sN;     /* element strides of Q                  */
+  int64_t kB, kH, kN;     /* element strides of K and V            */
+  int32_t Nk;             /* key / value tokens                    */
   const int32_t* rows;
   int32_t n_rows;
   int32_t chunks_per_head, rows_per_chunk;
@@ -324,11 +326,11 @@ typedef struct {
 static void load_head_kv(const attn_ctx* c, int64_t b, int64_t h, double* K, double* V, float* buf,
                          uint8_t* codes, double* blk) {
   const oracle_attn_cfg* g = c->cfg;
-  const int N = g->N, d = g->d;
-  const uint16_t* kb = c->k + b * c->sB + h * c->sH;
-  const uint16_t* vb = c->v + b * c->sB + h * c->sH;
+  const int N = c->Nk, d = g->d;
+  const uint16_t* kb = c->k + b * c->kB + h * c->kH;
+  const uint16_t* vb = c->v + b * c->kB + h * c->kH;
   for (int j = 0; j < N; ++j) {
-    for (int i = 0; i < d; ++i) buf[i] = oracle_decode_half(kb[(int64_t)j * c->sN + i], g->dtype);
+    for (int i = 0; i < d; ++i) buf[i] = oracle_decode_half(kb[(int64_t)j * c->kN + i], g->dtype);
     if (g->rotate) oracle_hadamard_rotate_f32(buf, d);
     if (g->quant) {
       for (int kk = 0; kk < d / 32; ++kk) {
@@ -348,7 +350,7 @@ static void load_head_kv(const attn_ctx* c, int64_t b, int64_t h, double* K, dou
         uint8_t sb;
         for (int t = 0; t < 32; ++t) {
           int n = 32 * kb32 + t;
-          blk[t] = n < N ? (double)oracle_decode_half(vb[(int64_t)n * c->sN + ch], g->dtype) : 0.0;
+          blk[t] = n < N ? (double)oracle_decode_half(vb[(int64_t)n * c->kN + ch], g->dtype) : 0.0;
         }
         oracle_quantize_block(blk, 32, g->rule, g->q, &sb, codes);
         for (int t = 0; t < 32; ++t) {
@@ -359,7 +361,7 @@ static void load_head_kv(const attn_ctx* c, int64_t b, int64_t h, double* K, dou
   } else {
     for (int j = 0; j < N; ++j)
       for (int ch = 0; ch < d; ++ch)
-        V[(int64_t)j * d + ch] = (double)oracle_decode_half(vb[(int64_t)j * c->sN + ch], g->dtype);
+        V[(int64_t)j * d + ch] = (double)oracle_decode_half(vb[(int64_t)j * c->kN + ch], g->dtype);
   }
 }
 
@@ -434,7 +436,7 @@ static void quantize_p_block(const oracle_attn_cfg* g, const double* p, double* 
 static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
   const attn_ctx* c = (const attn_ctx*)vctx;
   const oracle_attn_cfg* g = c->cfg;
-  const int N = g->N, d = g->d, Bc = g->kv_tile;
+  const int N = c->Nk, d = g->d, Bc = g->kv_tile;  /* N: keys of the row */
   const int T = (N + Bc - 1) / Bc;
   const int64_t bh = item / c->chunks_per_head;
   const int chunk = (int)(item % c->chunks_per_head);
@@ -604,6 +606,11 @@ int oracle_attention(const oracle_attn_cfg* cfg,
   if (cfg->p_mode < 0 || cfg->p_mode > 3) return -1;
   if (!rows) n_rows = cfg->N;
   if (n_rows < 1) return -1;
+  /* cross-attention: Nk keys and values; causal masking needs Nk = N, and
+   * caller strides describe one shape, so they need Nk = N too */
+  const int Nk = cfg->Nk > 0 ? cfg->Nk : cfg->N;
+  if (cfg->Nk < 0 || (Nk != cfg->N && (cfg->causal || strides))) return -1;
+  if (!shape_ok(cfg->B, cfg->H, Nk, cfg->d)) return -1;
   if (rows)
     for (int r = 0; r < n_rows; ++r)
       if (rows[r] < 0 || rows[r] >= cfg->N) return -1;
@@ -612,6 +619,8 @@ int oracle_attention(const oracle_attn_cfg* cfg,
   c.cfg = cfg;
   c.q = q; c.k = k; c.v = v;
   strides_or_contig(strides, cfg->H, cfg->N, cfg->d, &c.sB, &c.sH, &c.sN);
+  strides_or_contig(strides, cfg->H, Nk, cfg->d, &c.kB, &c.kH, &c.kN);
+  c.Nk = Nk;
   c.rows = rows;
   c.n_rows = n_rows;
   c.out = out; c.m_out = m_out; c.l_out = l_out; c.rowsum = rowsum; c.amb = amb;
@@ -623,7 +632,7 @@ int oracle_attention(const oracle_attn_cfg* cfg,
   if (cph > n_rows) cph = n_rows;
   c.chunks_per_head = cph;
   c.rows_per_chunk = (n_rows + cph - 1) / cph;
-  const int N = cfg->N, d = cfg->d, T = (N + cfg->kv_tile - 1) / cfg->kv_tile;
+  const int N = Nk, d = cfg->d, T = (N + cfg->kv_tile - 1) / cfg->kv_tile;
   size_t scratch = sizeof(double) * ((size_t)2 * N * d + 4 * (size_t)d + N + 3 * (size_t)T * cfg->kv_tile +
                                      3 * (size_t)T + 32) +
                    sizeof(float) * d + 64;

@@ -119,11 +119,14 @@ typedef struct {
   int32_t nthreads;
   double q;            /* boundary for the *_Q rules                        */
   double amb_delta;    /* relative decision margin for the allowance; 0=off */
+  int32_t Nk;          /* key/value tokens (cross-attention); 0 means N.
+                          Nk != N needs causal = 0 and contiguous inputs   */
 } oracle_attn_cfg;
 
-/* Attention forward [P1 Alg. 2; Eqs. 2-8 and 44-48].  For every head and
- * every listed query row (`rows`, n_rows indices shared by all heads; NULL
- * means all N rows) it writes
+/* Attention forward [P1 Alg. 2; Eqs. 2-8 and 44-48].  Q holds N query rows
+ * per head; K and V hold cfg->Nk (or N) tokens.  For every head and every
+ * listed query row (`rows`, n_rows indices shared by all heads; NULL means
+ * all N rows) it writes
  *   out      [B][H][n_rows][d]  the output row O_i
  *   m_out    [B][H][n_rows]     final running max (in S units), nullable
  *   l_out    [B][H][n_rows]     final l (for POSTNORM: the exact softmax

@@ -565,11 +565,12 @@ def test_result_depends_on_tile_width_but_stays_normalized():
 def brute_force_pnq(qh, kh, vh, Bc, causal, rule=oracle.RULE_UOS, direct=False):
     """Independent small re-statement of Alg. 2: materialize S, walk the tiles,
     quantize each aligned 32-key block of exp(S - m_new) with the (separately
-    pinned) block quantizer."""
-    N, d = qh.shape
+    pinned) block quantizer.  qh has Nq rows, kh and vh Nk rows."""
+    Nq, d = qh.shape
+    N = kh.shape[0]
     S = qh @ kh.T / math.sqrt(d)
-    out = np.zeros((N, d))
-    for i in range(N):
+    out = np.zeros((Nq, d))
+    for i in range(Nq):
         m, l, o = -np.inf, 0.0, np.zeros(d)
         for j0 in range(0, N, Bc):
             vis = [j for j in range(j0, min(j0 + Bc, N)) if (not causal or j <= i)]
@@ -641,3 +642,64 @@ def test_absmass_equals_output_for_nonnegative_values():
         assert np.allclose(r["absmass"], r["out"], rtol=1e-14, atol=0)
         r2 = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, p_mode=mode)
         assert (r2["absmass"] >= np.abs(r2["out"]) * (1 - 1e-14)).all()
+
+
+# --------------------------------------------------------------------------
+# cross-attention: Nq query rows against Nk key/value tokens [P1 Sec. 5.1,
+# Wan2.2's separate cross-attention; Alg. 2 with the key loop over Nk tokens]
+
+
+def cross_inputs(Nq, Nk, d, seed, scale=2.0):
+    xq = W.custom(1, 2, Nq, d, seed=seed, scale=scale)
+    xkv = W.custom(1, 2, Nk, d, seed=seed + 1000, scale=scale)
+    return xq["q"], xkv["k"], xkv["v"]
+
+
+@pytest.mark.parametrize("Nq,Nk", [(1, 300), (100, 7), (257, 33), (40, 129)])
+def test_cross_attention_unquantized_is_softmax_attention(Nq, Nk):
+    """Quantization off: the tiled recurrence over Nk keys equals the plain
+    softmax attention of Eq. 1 with a rectangular score matrix."""
+    d = 64
+    q, k, v = cross_inputs(Nq, Nk, d, seed=Nq * 7 + Nk)
+    for Bc in (32, 128):
+        r = oracle.attention(q, k, v, W.BF16, 1, 2, Nq, d, rotate=False, quant=False, kv_tile=Bc, Nk=Nk)
+        for h in range(2):
+            ref = exact_attention(*(W.from_bits(x[0, h], W.BF16).astype(np.float64) for x in (q, k, v)), False)
+            assert np.allclose(r["out"][0, h], ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("Nq,Nk,Bc", [(5, 70, 32), (37, 9, 32), (20, 130, 64)])
+def test_cross_attention_brute_force_tiny(Nq, Nk, Bc):
+    d = 32
+    xq = W.custom(1, 1, Nq, d, seed=Nq + Bc, scale=2.0)
+    xkv = W.custom(1, 1, Nk, d, seed=Nk + Bc + 500, scale=2.0)
+    cq, sq = oracle.quantize_rows(xq["q"], W.BF16, 1, 1, Nq, d, rotate=True)
+    qh = dequant_rows(cq, sq)
+    _, kh, vh = quantized_head(xkv["q"], xkv["k"], xkv["v"], W.BF16, Nk, d)
+    for direct in (False, True):
+        ref = brute_force_pnq(qh, kh, vh, Bc, False, direct=direct)
+        r = oracle.attention(xq["q"], xkv["k"], xkv["v"], W.BF16, 1, 1, Nq, d, kv_tile=Bc, Nk=Nk,
+                             p_mode=oracle.P_DIRECT if direct else oracle.P_PNQ)
+        assert np.allclose(r["out"][0, 0], ref, rtol=1e-12, atol=1e-12)
+        r1 = oracle.attention(xq["q"], xkv["k"], xkv["v"], W.BF16, 1, 1, Nq, d, kv_tile=Bc, Nk=Nk)
+        assert np.abs(r1["rowsum"] - 1).max() < 1e-12
+
+
+def test_cross_rows_equal_rows_of_a_self_attention_problem():
+    """Each query row is independent: embedding the Nq queries among Nk rows
+    of a self-attention problem over the same K, V gives the same rows."""
+    Nq, Nk, d = 19, 150, 64
+    q, k, v = cross_inputs(Nq, Nk, d, seed=3)
+    qbig = W.custom(1, 2, Nk, d, seed=9, scale=2.0)["q"].copy()
+    pos = np.arange(Nq) * 7 + 3
+    qbig[:, :, pos] = q
+    cross = oracle.attention(q, k, v, W.BF16, 1, 2, Nq, d, Nk=Nk)
+    selfr = oracle.attention(qbig, k, v, W.BF16, 1, 2, Nk, d, rows=pos)
+    for key in ("out", "m", "l", "rowsum"):
+        assert np.array_equal(cross[key], selfr[key])
+
+
+def test_cross_attention_argument_checks():
+    q, k, v = cross_inputs(8, 16, 32, seed=1)
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, W.BF16, 1, 2, 8, 32, Nk=16, causal=True)
