@@ -149,6 +149,7 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     B, H, N, d = w.shape
+    Nk = w.kv_tokens  # key/value tokens (N unless cross-attention)
     log(f"workload {args.workload}: {w.name} {w.describe()}; generating inputs")
     t0 = time.perf_counter()
     dev = {}
@@ -161,8 +162,8 @@ def main():
 
     stream = torch.cuda.current_stream()
     qm = mx.MXTensor.empty(B, H, N, d, mx.AXIS_HEAD_DIM)
-    km = mx.MXTensor.empty(B, H, N, d, mx.AXIS_HEAD_DIM)
-    vm = mx.MXTensor.empty(B, H, N, d, mx.AXIS_TOKEN)
+    km = mx.MXTensor.empty(B, H, Nk, d, mx.AXIS_HEAD_DIM)
+    vm = mx.MXTensor.empty(B, H, Nk, d, mx.AXIS_TOKEN)
     out = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -197,7 +198,7 @@ def main():
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
-    quant_bytes = 3 * B * H * N * d * QUANT_BYTES_PER_ELEMENT
+    quant_bytes = B * H * (N + 2 * Nk) * d * QUANT_BYTES_PER_ELEMENT
     quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
 
     result = {
@@ -215,7 +216,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: {w.describe()}, one step = rotate+quantize Q, K; quantize V; "
                                f"fused PNQ forward", "B": B, "H": H, "N": N, "d": d,
-                   "causal": w.causal, "kv_tile": mx.forward_kv_tile(d, w.causal)},
+                   "causal": w.causal, "kv_tile": mx.forward_kv_tile(d, w.causal),
+                   **({"Nk": Nk} if Nk != N else {})},
         "forward": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
                     "frac_mfma_peak": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4)},
         "quantizer": {"ms": round(quant_ms, 4), "gb_per_s": round(quant_gbs, 1),
@@ -223,9 +225,9 @@ def main():
                       "bytes": quant_bytes},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(flops)},
+                     "traffic": measured_traffic(flops) if args.workload == 2 else None},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and Nk == N and not w.causal:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(result), flush=True)

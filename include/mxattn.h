@@ -149,14 +149,21 @@ mxattn_status mxattn_rotate_quantize(const void* x, int32_t dtype, mxattn_shape 
                                      int32_t rule, mxattn_mx_tensor* out, hipStream_t stream);
 
 /* Fused MXFP4 attention forward with PNQ (Alg. 2 steps 8-22).
- *   q, k     head-dimension MXFP4 tensors of one shape, both rotated or both
- *            not (Q K^T is unchanged by the rotation only if both are)
- *   v        token-axis MXFP4 tensor of the same shape
- *   causal   1: key j is visible to query i iff j <= i
- *   out      device float [B, H, N, d], contiguous: O = diag(l)^-1 O~ (Eq. 8)
- *   row_stats device float [B, H, N, 2] or NULL: (m, l) per row, with m the
- *            final running maximum of S = Q^ K^T / sqrt(d) and l the final
- *            PNQ row sum (l >= 1, App. J)
+ *   q        head-dimension MXFP4 tensor, shape [B, H, Nq, d]
+ *   k        head-dimension MXFP4 tensor, shape [B, H, Nk, d]; both q and k
+ *            rotated or both not (Q K^T is unchanged by the rotation only if
+ *            both are)
+ *   v        token-axis MXFP4 tensor of the shape of k
+ *            Nk != Nq is cross-attention, as in the separate text
+ *            cross-attention of the video models the pages evaluate
+ *            (Sec. 5.1); the key loop then runs over the Nk tokens
+ *   causal   1: key j is visible to query i iff j <= i (needs Nk = Nq,
+ *            else MXATTN_ERR_MISMATCH)
+ *   out      device float [B, H, Nq, d], contiguous: O = diag(l)^-1 O~
+ *            (Eq. 8)
+ *   row_stats device float [B, H, Nq, 2] or NULL: (m, l) per row, with m
+ *            the final running maximum of S = Q^ K^T / sqrt(d) and l the
+ *            final PNQ row sum (l >= 1, App. J)
  * S, l and O~ accumulate in binary32.  The exponential tile is quantized
  * with the UOS rule whatever the rule of the inputs. */
 mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* k,

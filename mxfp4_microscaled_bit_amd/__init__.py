@@ -179,7 +179,8 @@ def rotate_quantize(x: torch.Tensor, axis: int = AXIS_HEAD_DIM, rotate: bool = T
 
 def forward(q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: torch.Tensor | None = None,
             row_stats: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """mxattn_forward; returns O as float32 [B, H, N, d]."""
+    """mxattn_forward; returns O as float32 [B, H, Nq, d] (Nq = q's tokens; k and v
+    may hold another token count: cross-attention)."""
     B, H, N, d = q.shape
     if out is None:
         out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.codes.device)

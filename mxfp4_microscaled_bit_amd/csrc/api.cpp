@@ -133,9 +133,13 @@ mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* 
   if (st != MXATTN_OK) return st;
   st = check_mx(v, MXATTN_AXIS_TOKEN);
   if (st != MXATTN_OK) return st;
-  if (!same_shape(q->shape, k->shape) || !same_shape(q->shape, v->shape)) return MXATTN_ERR_MISMATCH;
+  // K^ and V^ share one shape; Q^ may have another token count
+  // (cross-attention) but the same B, H and d
+  if (!same_shape(k->shape, v->shape)) return MXATTN_ERR_MISMATCH;
+  if (q->shape.B != k->shape.B || q->shape.H != k->shape.H || q->shape.d != k->shape.d) return MXATTN_ERR_MISMATCH;
   if ((q->rotated != 0) != (k->rotated != 0)) return MXATTN_ERR_MISMATCH;
   if (causal != 0 && causal != 1) return MXATTN_ERR_ENUM;
+  if (causal && q->shape.N != k->shape.N) return MXATTN_ERR_MISMATCH;
   if (!aligned16(out) || (row_stats && !aligned16(row_stats))) return MXATTN_ERR_ALIGN;
 
   AttnArgs a;
@@ -143,6 +147,7 @@ mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* 
   a.kc = k->codes; a.ks = k->scales;
   a.vc = v->codes; a.vs = v->scales;
   a.B = q->shape.B; a.H = q->shape.H; a.N = q->shape.N; a.d = q->shape.d;
+  a.Nk = k->shape.N;
   a.causal = causal;
   a.mode = kModePnq;
   a.rule = MXATTN_SCALE_UOS;
@@ -203,6 +208,7 @@ mxattn_status mxattn_quantize_reference_modes(const void* q, const void* k, cons
   a.kc = tk.codes; a.ks = tk.scales;
   a.vc = tv.codes; a.vs = tv.scales;
   a.B = shape.B; a.H = shape.H; a.N = shape.N; a.d = shape.d;
+  a.Nk = shape.N;
   a.causal = causal;
   a.mode = p_mode == MXATTN_P_PNQ ? kModePnq : (p_mode == MXATTN_P_DIRECT ? kModeDirect : kModePostnorm);
   a.rule = rule;

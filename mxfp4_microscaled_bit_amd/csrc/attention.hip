@@ -67,7 +67,10 @@ struct Params {
   float* row_stats;
   float* row_sums;
   float* stats;
-  int H, N, Np, nqt;
+  int H;
+  int N, Np;    // keys / values: count and padded count
+  int Nq, Nqp;  // queries: count and padded count
+  int nqt;      // query tiles per head
 };
 
 // byte offsets inside one LDS stage
@@ -508,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   // Q^ operand (B operand of S^T: lane = query L%32, d-chunk 2h + L/32 in
   // step h) and its scales (byte h = d-block 2h + L/32)
   const int qi = qt * kBr + 32 * wave + r;
-  const int64_t qrow = bh * p.Np + qi;
+  const int64_t qrow = bh * p.Nqp + qi;
   uint4 qop[NH];
   int qsc;
 #pragma unroll
@@ -589,14 +592,14 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
     keep_live(done, held[0], held[1], held[2], held[3]);
     keep_live(done, one_sc);
   }
-  if (qi >= p.N) return;
+  if (qi >= p.Nq) return;
   // O = O~ / l with a correctly rounded division (Eq. 8): with V^ constant
   // per channel, O~ = v^ l exactly, and the division returns v^ exactly
   float l;
   if constexpr (MODE == kModePnq) l = lsum;
   else if constexpr (MODE == kModeDirect) l = rs.l;
   else l = 1.0f;
-  float* orow = p.out + (bh * p.N + qi) * D + 4 * g;
+  float* orow = p.out + (bh * p.Nq + qi) * D + 4 * g;
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
@@ -607,10 +610,10 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
     }
   if (g == 0) {
     if (p.row_stats) {
-      p.row_stats[(bh * p.N + qi) * 2 + 0] = rs.m * F::kInvSqrtD;
-      p.row_stats[(bh * p.N + qi) * 2 + 1] = l;
+      p.row_stats[(bh * p.Nq + qi) * 2 + 0] = rs.m * F::kInvSqrtD;
+      p.row_stats[(bh * p.Nq + qi) * 2 + 1] = l;
     }
-    if (p.row_sums) p.row_sums[bh * p.N + qi] = (MODE == kModePostnorm) ? lsum : lsum / l;
+    if (p.row_sums) p.row_sums[bh * p.Nq + qi] = (MODE == kModePostnorm) ? lsum : lsum / l;
   }
 }
 
@@ -646,9 +649,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   prm.row_sums = a.row_sums;
   prm.stats = a.stats_ws;
   prm.H = a.H;
-  prm.N = a.N;
-  prm.Np = (int)padded_tokens(a.N);
-  prm.nqt = prm.Np / kBr;
+  prm.N = a.Nk;
+  prm.Np = (int)padded_tokens(a.Nk);
+  prm.Nq = a.N;
+  prm.Nqp = (int)padded_tokens(a.N);
+  prm.nqt = prm.Nqp / kBr;
   if (a.d == 128) return a.causal ? dispatch_mode<128, true>(a, prm, stream) : dispatch_mode<128, false>(a, prm, stream);
   return a.causal ? dispatch_mode<64, true>(a, prm, stream) : dispatch_mode<64, false>(a, prm, stream);
 }

@@ -39,7 +39,8 @@ struct AttnArgs {
   const uint8_t* ks;
   const uint8_t* vc;
   const uint8_t* vs;
-  int B, H, N, d;
+  int B, H, N, d;  // N: query rows
+  int Nk;           // key / value tokens (cross-attention); N for self-attention
   int causal;
   int mode;  // AttnMode
   int rule;  // scale rule of the softmax-path quantizer

@@ -103,7 +103,10 @@ def test_forward_rejects_bad_arguments():
     assert fwd(q=_desc(0, codes=None)) == 1
     assert fwd(k=_desc(1)) == 6          # K must be head-dim blocked
     assert fwd(v=_desc(0)) == 6          # V must be token blocked
-    assert fwd(k=_desc(0, N=65)) == 6    # shapes disagree
+    assert fwd(k=_desc(0, N=65)) == 6    # K and V shapes disagree
+    assert fwd(k=_desc(0, N=65), v=_desc(1, N=65), causal=1) == 6  # causal cross-attention
+    assert fwd(k=_desc(0, H=2), v=_desc(1, H=2)) == 6  # heads disagree
+    assert fwd(k=_desc(0, d=128), v=_desc(1, d=128)) == 6  # head dims disagree
     assert fwd(k=_desc(0, rotated=0)) == 6  # Q rotated, K not
     assert fwd(v=_desc(1, d=96)) == 2
     assert fwd(causal=2) == 8

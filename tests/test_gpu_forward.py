@@ -31,7 +31,7 @@ def _oracle_heads(w, heads, rows, p_mode=oracle.P_PNQ, rule=oracle.RULE_UOS, rot
                W.generate(w, t, heads=heads)[None]) for t in "qkv"}
     return oracle.attention(sel["q"], sel["k"], sel["v"], w.dtype, 1, len(heads), w.N, w.d, causal=w.causal,
                             rotate=rotate, rule=rule, p_mode=p_mode, kv_tile=KV_TILE, rows=rows,
-                            amb_delta=DELTA)
+                            amb_delta=DELTA, Nk=w.kv_tokens)
 
 
 def _gpu_rows(out, heads, rows):
@@ -46,10 +46,11 @@ WORKLOAD_SAMPLING = {
     4: ([(0, 0), (1, 17), (3, 31)], 60),
     2: ([(0, 0), (0, 19), (0, 39)], 40),
     3: ([(0, 0), (0, 23)], 16),
+    6: ([(0, 0), (0, 21), (0, 39)], 200),
 }
 
 
-@pytest.mark.parametrize("cid", [1, 5, 4, 2, 3])
+@pytest.mark.parametrize("cid", [1, 5, 4, 2, 3, 6])
 def test_forward_matches_oracle(cid):
     w = W.WORKLOADS[cid]
     B, H, N, d = w.shape
@@ -65,7 +66,7 @@ def test_forward_matches_oracle(cid):
         rows = _sample_rows(N, nrand, cid, w.causal)
     ref = _oracle_heads(w, heads, rows, bits=bits)
     gpu = _gpu_rows(out, heads, rows)
-    n_tiles = (N + KV_TILE - 1) // KV_TILE
+    n_tiles = (w.kv_tokens + KV_TILE - 1) // KV_TILE
     check_output(gpu, ref, f"workload {cid} PNQ", n_tiles)
     st = _gpu_rows(stats, heads, rows)
     # App. J: l >= 1 for every row; l and m agree with the oracle
@@ -135,6 +136,43 @@ def test_ragged_and_tiny_shapes(N, d, causal):
                            amb_delta=DELTA)
     check_output(out.cpu().numpy(), ref, f"N={N} d={d} causal={causal}", (N + KV_TILE - 1) // KV_TILE)
     assert (stats.cpu().numpy()[..., 1] >= 1.0).all()
+
+
+@pytest.mark.parametrize("Nq,Nk,d", [(300, 77, 128), (1000, 512, 128), (129, 1, 64), (5, 700, 128),
+                                     (256, 128, 64), (131, 4100, 128)])
+def test_cross_attention_matches_oracle(Nq, Nk, d):
+    """Cross-attention: Nq query rows against Nk key/value tokens (ragged on
+    both sides, a single key, fewer keys than one tile, many tiles)."""
+    say(f"cross-attention Nq={Nq} Nk={Nk} d={d}")
+    B, H = 2, 3
+    xq = W.custom(B, H, Nq, d, seed=Nq + d, scale=2.0)
+    xkv = W.custom(B, H, Nk, d, seed=Nk + 7 * d, scale=2.0)
+    out, stats = run_forward(to_device(xq["q"], W.BF16), to_device(xkv["k"], W.BF16), to_device(xkv["v"], W.BF16),
+                             False)
+    assert tuple(out.shape) == (B, H, Nq, d)
+    ref = oracle.attention(xq["q"], xkv["k"], xkv["v"], W.BF16, B, H, Nq, d, kv_tile=KV_TILE, amb_delta=DELTA,
+                           Nk=Nk)
+    check_output(out.cpu().numpy(), ref, f"cross Nq={Nq} Nk={Nk} d={d}", (Nk + KV_TILE - 1) // KV_TILE)
+    st = stats.cpu().numpy()
+    assert (st[..., 1] >= 1.0).all()
+    assert np.allclose(st[..., 0], ref["m"], rtol=1e-5, atol=1e-5)
+
+
+def test_cross_attention_rows_equal_self_attention_rows():
+    """Every query row is independent of the others: placing the Nq queries
+    among the rows of a self-attention problem over the same K^, V^ gives the
+    same output rows bit for bit."""
+    B, H, Nq, Nk, d = 1, 2, 77, 600, 128
+    xq = W.custom(B, H, Nq, d, seed=21, scale=2.0)
+    xkv = W.custom(B, H, Nk, d, seed=22, scale=2.0)
+    big = W.custom(B, H, Nk, d, seed=23, scale=2.0)["q"].copy()
+    pos = np.arange(Nq) * 7 + 5
+    big[:, :, pos] = xq["q"]
+    dk, dv = to_device(xkv["k"], W.BF16), to_device(xkv["v"], W.BF16)
+    cross, _ = run_forward(to_device(xq["q"], W.BF16), dk, dv, False)
+    selfo, _ = run_forward(to_device(big, W.BF16), dk, dv, False)
+    say("cross rows vs self-attention rows")
+    assert torch.equal(cross, selfo[:, :, torch.from_numpy(pos).long().cuda()])
 
 
 def test_fp16_inputs():

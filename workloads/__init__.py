@@ -16,7 +16,10 @@ Recipe (identical for every workload):
 
 Shapes follow the pages' workloads: self-attention of video diffusion
 transformers (Wan2.2-like and HunyuanVideo-like token counts), a causal
-language-model shape, and a small-head stress case.  None of the pages'
+language-model shape, and a small-head stress case.  The pages also mention
+Wan2.2's separate text cross-attention without giving its shape; the cross
+workload pairs the Wan-like video queries with 512 text keys/values, a
+synthetic choice.  None of the pages'
 model activations are available, so lognormal channel scales and sparse x15
 outlier channels stand in for the activation outliers the pages describe.
 """
@@ -45,18 +48,26 @@ class Workload:
     seed: int
     kind: str
     params: dict = field(default_factory=dict)
+    Nk: int = 0  # key/value tokens of cross-attention; 0: self-attention (N)
 
     @property
     def shape(self):
         return (self.B, self.H, self.N, self.d)
 
+    @property
+    def kv_tokens(self) -> int:
+        return self.Nk if self.Nk > 0 else self.N
+
+    def tokens(self, tensor: str) -> int:
+        return self.N if tensor == "q" else self.kv_tokens
+
     def flops(self) -> float:
         """4*d flops per visible (query, key) pair: QK^T and PV each take 2*d."""
-        pairs = self.N * (self.N + 1) / 2 if self.causal else float(self.N) * self.N
+        pairs = self.N * (self.N + 1) / 2 if self.causal else float(self.N) * self.kv_tokens
         return 4.0 * self.d * self.B * self.H * pairs
 
     def describe(self) -> str:
-        return (f"B{self.B} H{self.H} N{self.N} d{self.d} "
+        return (f"B{self.B} H{self.H} N{self.N}{f' Nk{self.Nk}' if self.Nk else ''} d{self.d} "
                 f"{'fp16' if self.dtype == FP16 else 'bf16'}{' causal' if self.causal else ''}")
 
 
@@ -71,6 +82,8 @@ WORKLOADS = {
                 {"sigma": 1.0}),
     5: Workload(5, "sharp_d64", 16, 16, 4096, 64, BF16, False, 5, "sharp",
                 {"qk_scale": 4.0, "v_range": 8.0}),
+    6: Workload(6, "wan_like_cross", 1, 40, 32760, 128, BF16, False, 6, "lognormal",
+                {"sigma": 1.0}, Nk=512),
 }
 
 TENSOR_ID = {"q": 0, "k": 1, "v": 2}
@@ -133,7 +146,7 @@ def head_values(w: Workload, tensor: str, b: int, h: int, scales=None, out=None)
     t = TENSOR_ID[tensor]
     rng = _rng(w.seed, t, b, h)
     if out is None:
-        out = np.empty((w.N, w.d))
+        out = np.empty((w.tokens(tensor), w.d))
     if w.kind == "sharp":
         if tensor == "v":
             r = w.params["v_range"]
@@ -176,22 +189,24 @@ def _scratch(shape):
 def generate(w: Workload, tensor: str, heads=None) -> np.ndarray:
     """16-bit patterns of one input tensor.
 
-    heads=None -> array [B, H, N, d]; heads=[(b, h), ...] -> array [len(heads), N, d].
+    heads=None -> array [B, H, n, d]; heads=[(b, h), ...] -> array [len(heads), n, d],
+    with n = w.tokens(tensor).
     """
     scales = channel_scales(w, tensor)
+    n = w.tokens(tensor)
     sel = [(b, h) for b in range(w.B) for h in range(w.H)] if heads is None else list(heads)
-    out = np.empty((len(sel), w.N, w.d), np.uint16)
+    out = np.empty((len(sel), n, w.d), np.uint16)
 
     def one(i):
         b, h = sel[i]
-        f64, f32 = _scratch((w.N, w.d))
+        f64, f32 = _scratch((n, w.d))
         head_values(w, tensor, b, h, scales, out=f64)
         to_bits(f64, w.dtype, out=out[i], scratch=f32)
 
     with ThreadPoolExecutor(max_workers=_threads()) as ex:
         list(ex.map(one, range(len(sel))))
     if heads is None:
-        return out.reshape(w.B, w.H, w.N, w.d)
+        return out.reshape(w.B, w.H, n, w.d)
     return out
 
 
