@@ -56,6 +56,11 @@ def _load():
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_scale_sweep.restype = ctypes.c_int
+    lib.oracle_scale_sweep.argtypes = [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int,
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_quantize_token_blocks.restype = ctypes.c_int
     lib.oracle_quantize_token_blocks.argtypes = [
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -189,6 +194,27 @@ def quantize_token_blocks(x_bits, dtype, B, H, N, d, *, rule=RULE_UOS, q=0.0, bl
     if rc != 0:
         raise ValueError("oracle_quantize_token_blocks rejected its arguments")
     return codes, scales
+
+
+def scale_sweep(x_bits, dtype, B, H, N, d, qs, *, axis=AXIS_HEAD_DIM, rotate=False, heads=None,
+                strides=None, nthreads=None):
+    """Per-head sum of squared MXFP4 quantization errors for each boundary in
+    ``qs`` (rule e = ceil(log2(M/q))).  ``heads``: indices b*H+h or None for all.
+    Returns float64 [n_heads, len(qs)]."""
+    x_bits = np.asarray(x_bits)
+    assert x_bits.dtype == np.uint16
+    if strides is None:
+        x_bits = np.ascontiguousarray(x_bits)
+    qa = np.ascontiguousarray(np.asarray(qs, dtype=np.float64))
+    hd = None if heads is None else np.ascontiguousarray(np.asarray(heads, dtype=np.int64))
+    nh = B * H if hd is None else hd.size
+    sse = np.empty((nh, qa.size), np.float64)
+    rc = _load().oracle_scale_sweep(_ptr(x_bits), dtype, B, H, N, d, _ptr(_strides(strides)), axis,
+                                    int(bool(rotate)), _ptr(qa), qa.size, _ptr(hd), nh, _ptr(sse),
+                                    nthreads or default_threads())
+    if rc != 0:
+        raise ValueError("oracle_scale_sweep rejected its arguments")
+    return sse
 
 
 def attention(q_bits, k_bits, v_bits, dtype, B, H, N, d, *, causal=False, rotate=True,

@@ -308,6 +308,78 @@ int oracle_quantize_token_blocks(const uint16_t* x, int dtype, int B, int H, int
 }
 
 /* ------------------------------------------------------------------ */
+/* Q_max sweep                                                          */
+
+typedef struct {
+  const uint16_t* x;
+  int dtype, B, H, N, d, axis, rotate, n_q;
+  const double* qs;
+  int64_t sB, sH, sN;
+  const int64_t* heads;
+  double* sse;
+} sweep_ctx;
+
+/* squared error of one block quantized with e = ceil(log2(M/q)), added to acc */
+static double block_sse(const double* blk, double q) {
+  uint8_t codes[32], sb;
+  oracle_quantize_block(blk, 32, ORACLE_RULE_CEIL_Q, q, &sb, codes);
+  double s = 0.0;
+  for (int i = 0; i < 32; ++i) {
+    const double r = blk[i] - dequant(codes[i], sb);
+    s += r * r;
+  }
+  return s;
+}
+
+/* One head: every block of the tensor the quantizer sees, in row (or token
+ * block, then channel) order, each quantized once per boundary q_j. */
+static void sweep_item(void* ctx, int64_t it, void* scratch) {
+  const sweep_ctx* c = (const sweep_ctx*)ctx;
+  const int64_t bh = c->heads ? c->heads[it] : it;
+  const int64_t b = bh / c->H, h = bh % c->H;
+  const uint16_t* base = c->x + b * c->sB + h * c->sH;
+  double* out = c->sse + it * c->n_q;
+  float* buf = (float*)scratch;
+  double blk[32];
+  for (int j = 0; j < c->n_q; ++j) out[j] = 0.0;
+  if (c->axis == ORACLE_AXIS_HEAD_DIM) {
+    for (int n = 0; n < c->N; ++n) {
+      for (int i = 0; i < c->d; ++i) buf[i] = oracle_decode_half(base[n * c->sN + i], c->dtype);
+      if (c->rotate) oracle_hadamard_rotate_f32(buf, c->d);
+      for (int k = 0; k < c->d / 32; ++k) {
+        for (int i = 0; i < 32; ++i) blk[i] = (double)buf[32 * k + i];
+        for (int j = 0; j < c->n_q; ++j) out[j] += block_sse(blk, c->qs[j]);
+      }
+    }
+  } else {
+    for (int kb = 0; kb < (c->N + 31) / 32; ++kb)
+      for (int ch = 0; ch < c->d; ++ch) {
+        for (int t = 0; t < 32; ++t) {
+          const int64_t n = 32 * kb + t;
+          blk[t] = n < c->N ? (double)oracle_decode_half(base[n * c->sN + ch], c->dtype) : 0.0;
+        }
+        for (int j = 0; j < c->n_q; ++j) out[j] += block_sse(blk, c->qs[j]);
+      }
+  }
+}
+
+int oracle_scale_sweep(const uint16_t* x, int dtype, int B, int H, int N, int d,
+                       const int64_t* strides, int axis, int rotate, const double* qs, int n_q,
+                       const int64_t* heads, int64_t n_heads, double* sse, int nthreads) {
+  if (!x || !qs || !sse || !shape_ok(B, H, N, d) || n_q < 1 || n_heads < 0) return -1;
+  if (axis != ORACLE_AXIS_HEAD_DIM && axis != ORACLE_AXIS_TOKEN) return -1;
+  if (rotate && axis != ORACLE_AXIS_HEAD_DIM) return -1;
+  for (int j = 0; j < n_q; ++j)
+    if (!(qs[j] > 0.0) || !isfinite(qs[j])) return -1;
+  sweep_ctx c = {x, dtype, B, H, N, d, axis, rotate, n_q, qs, 0, 0, 0, heads, sse};
+  strides_or_contig(strides, H, N, d, &c.sB, &c.sH, &c.sN);
+  if (heads)
+    for (int64_t r = 0; r < n_heads; ++r)
+      if (heads[r] < 0 || heads[r] >= (int64_t)B * H) return -1;
+  return run_pool(sweep_item, &c, n_heads, sizeof(float) * (size_t)d, nthreads);
+}
+
+/* ------------------------------------------------------------------ */
 /* attention                                                            */
 
 typedef struct {

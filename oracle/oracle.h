@@ -107,6 +107,18 @@ int oracle_quantize_token_blocks(const uint16_t* x, int dtype, int B, int H, int
                                  const int64_t* blocks, int64_t n_blocks,
                                  uint8_t* codes, uint8_t* scales, int nthreads);
 
+/* Scale-boundary sweep [P1 Sec. 5.5.1, Table 4; Eq. 13]: for each listed
+ * head (`heads`: indices b*H + h; NULL with n_heads = B*H means all in order)
+ * and each boundary q_j, the sum over the head's MXFP4 blocks of
+ * sum_i (x_i - x^_i)^2, where x is what the quantizer sees (the decoded input,
+ * Hadamard-rotated in binary32 if `rotate`) and x^ its MXFP4 reconstruction
+ * with e = ceil(log2(M / q_j)).  axis HEAD_DIM: 32-channel blocks of a row;
+ * axis TOKEN: 32-token blocks of a channel, tokens past N counting as +0.
+ * sse: [n_heads][n_q] binary64.  Returns 0, or -1 on a bad argument. */
+int oracle_scale_sweep(const uint16_t* x, int dtype, int B, int H, int N, int d,
+                       const int64_t* strides, int axis, int rotate, const double* qs, int n_q,
+                       const int64_t* heads, int64_t n_heads, double* sse, int nthreads);
+
 typedef struct {
   int32_t B, H, N, d;
   int32_t dtype;

@@ -703,3 +703,67 @@ def test_cross_attention_argument_checks():
     q, k, v = cross_inputs(8, 16, 32, seed=1)
     with pytest.raises(ValueError):
         oracle.attention(q, k, v, W.BF16, 1, 2, 8, 32, Nk=16, causal=True)
+
+
+# --------------------------------------------------------------------------
+# Q_max sweep  [P1 Sec. 5.5.1, Table 4; Eq. 13; App. G]
+
+
+def test_sweep_closed_form_block_at_the_uos_boundary():
+    """Every value of a block equal to 7.25 * 2^-3 = 0.90625 (exact in bf16):
+    for q >= 7.25 the scale is 2^-3 (a tie M = q 2^e keeps the smaller e) and
+    7.25 saturates to 6, an error of 1.25 * 2^-3 per element; for q < 7.25 the
+    scale doubles and 3.625 rounds up to 4, an error of 0.75 * 2^-3."""
+    B, H, N, d = 1, 2, 32, 64
+    x = np.full((B, H, N, d), W.to_bits(np.array(0.90625), W.BF16), np.uint16)
+    qs = [6.0, 7.0, 7.2, 7.25, 7.3, 8.0]
+    per_block_hi = 32 * (1.25 / 8) ** 2
+    per_block_lo = 32 * (0.75 / 8) ** 2
+    for axis, nblocks in ((oracle.AXIS_TOKEN, d * (N // 32)), (oracle.AXIS_HEAD_DIM, N * d // 32)):
+        sse = oracle.scale_sweep(x, W.BF16, B, H, N, d, qs, axis=axis)
+        want = [nblocks * (per_block_hi if q >= 7.25 else per_block_lo) for q in qs]
+        assert np.array_equal(sse, np.array([want, want]))
+
+
+def test_sweep_equals_sum_of_squares_of_the_quantizers_errors():
+    """Wiring check against the two block quantizers: the sweep's per-head sum
+    equals sum (x - x^)^2 computed here from the oracle's own codes and scales
+    and the separately pinned rotation, for both axes and a ragged tail."""
+    B, H, N, d = 1, 2, 45, 64
+    x = W.custom(B, H, N, d, seed=31, scale=3.0)["q"]
+    qs = [6.0, 6.55, 7.25, 8.0]
+    grid = np.array([oracle.e2m1_magnitude(c) for c in range(8)])
+    # head-dim axis with rotation
+    sse = oracle.scale_sweep(x, W.BF16, B, H, N, d, qs, rotate=True)
+    xs = W.from_bits(x, W.BF16).reshape(-1, d).copy()
+    for r in range(xs.shape[0]):
+        xs[r] = oracle.hadamard_rotate_f32(xs[r])
+    for j, q in enumerate(qs):
+        c, s = oracle.quantize_rows(x, W.BF16, B, H, N, d, rotate=True, rule=oracle.RULE_CEIL_Q, q=q)
+        xh = grid[c & 7] * np.where(c & 8, -1.0, 1.0) * np.exp2(np.repeat(s.astype(np.float64) - 127, 32, axis=-1))
+        err = ((xs.astype(np.float64) - xh) ** 2).reshape(B * H, -1).sum(axis=1)
+        assert np.allclose(sse[:, j], err, rtol=1e-13, atol=0)
+    # token axis, tail tokens past N count as +0
+    sse = oracle.scale_sweep(x, W.BF16, B, H, N, d, qs, axis=oracle.AXIS_TOKEN)
+    NB = (N + 31) // 32
+    xv = np.zeros((B * H, NB * 32, d))
+    xv[:, :N] = W.from_bits(x, W.BF16).reshape(B * H, N, d)
+    for j, q in enumerate(qs):
+        c, s = oracle.quantize_token_blocks(x, W.BF16, B, H, N, d, rule=oracle.RULE_CEIL_Q, q=q)
+        xh = grid[c & 7] * np.where(c & 8, -1.0, 1.0) * np.exp2(s.astype(np.float64) - 127)[..., None]
+        xh = xh.reshape(B * H, NB, d, 32).transpose(0, 1, 3, 2).reshape(B * H, NB * 32, d)
+        err = ((xv - xh) ** 2).sum(axis=(1, 2))
+        assert np.allclose(sse[:, j], err, rtol=1e-13, atol=0)
+
+
+def test_sweep_head_selection_and_arguments():
+    B, H, N, d = 2, 3, 40, 32
+    x = W.custom(B, H, N, d, seed=32)["k"]
+    full = oracle.scale_sweep(x, W.BF16, B, H, N, d, [6.0, 7.25], rotate=True)
+    some = oracle.scale_sweep(x, W.BF16, B, H, N, d, [6.0, 7.25], rotate=True, heads=[5, 0])
+    assert np.array_equal(some, full[[5, 0]])
+    for bad in (dict(qs=[0.0]), dict(qs=[float("inf")]), dict(qs=[7.0], axis=oracle.AXIS_TOKEN, rotate=True),
+                dict(qs=[7.0], heads=[6])):
+        qs = bad.pop("qs")
+        with pytest.raises(ValueError):
+            oracle.scale_sweep(x, W.BF16, B, H, N, d, qs, **bad)
