@@ -57,8 +57,9 @@
  *     1, 2, 4, ..., d/2 (each output one correctly rounded add/subtract),
  *     then one multiply by fl32(1/sqrt(d)).
  *   - Block scale: M = max |x_i|; an all-zero block gets 2^0.  Otherwise UOS
- *     e = ceil(log2(M / 7.25)) or OCP e = floor(log2 M) - 2, clamped to
- *     [-127, 127].
+ *     e = ceil(log2(M / 7.25)), OCP e = floor(log2 M) - 2, or (the ceiling
+ *     family, mxattn_rotate_quantize_q) e = ceil(log2(M / q)), i.e. the
+ *     smallest e with M <= q 2^e, clamped to [-127, 127].
  *   - Elements: x_i / 2^e rounded to the nearest E2M1 value, ties to the even
  *     code, magnitudes above 6 saturating at 6; a value that rounds to zero
  *     keeps its sign bit.
@@ -90,9 +91,12 @@ typedef enum {
 
 typedef enum { MXATTN_BF16 = 0, MXATTN_FP16 = 1 } mxattn_dtype;
 typedef enum { MXATTN_AXIS_HEAD_DIM = 0, MXATTN_AXIS_TOKEN = 1 } mxattn_axis;
-/* Shared-scale rule: UOS (Sec. 4.1, Eq. 19 with q* = 7.25) or the OCP
- * floor rule used by the vanilla baseline (Sec. 2, Eq. 11; App. G Eq. 97). */
-typedef enum { MXATTN_SCALE_UOS = 0, MXATTN_SCALE_OCP = 1 } mxattn_scale_rule;
+/* Shared-scale rule: UOS (Sec. 4.1, Eq. 19 with q* = 7.25), the OCP floor
+ * rule used by the vanilla baseline (Sec. 2, Eq. 11; App. G Eq. 97), or the
+ * ceiling family e = ceil(log2(M / q)) with a caller-chosen boundary q
+ * (Eq. 13; q = 6 is TFS, Eq. 14; q = 7 the OAS-equivalent rule, App. G; UOS
+ * is q = 7.25).  CEIL_Q tensors come from mxattn_rotate_quantize_q. */
+typedef enum { MXATTN_SCALE_UOS = 0, MXATTN_SCALE_OCP = 1, MXATTN_SCALE_CEIL_Q = 2 } mxattn_scale_rule;
 /* Placement of the softmax-path quantizer (Sec. 4.2; Sec. 5.5.2):
  *   PNQ      l and O both updated from Q(P~)            (Eqs. 44-48)
  *   DIRECT   l from P~, O from Q(P~)                     (Eq. 42 / Eqs. 16-17)
@@ -101,6 +105,9 @@ typedef enum { MXATTN_SCALE_UOS = 0, MXATTN_SCALE_OCP = 1 } mxattn_scale_rule;
 typedef enum { MXATTN_P_PNQ = 0, MXATTN_P_DIRECT = 1, MXATTN_P_POSTNORM = 2 } mxattn_p_mode;
 
 #define MXATTN_TOKEN_ALIGN 128
+#define MXATTN_SWEEP_MAX 48   /* boundaries per mxattn_scale_sweep call     */
+#define MXATTN_Q_MIN 2.0      /* range of a ceiling-rule boundary q          */
+#define MXATTN_Q_MAX 64.0
 
 typedef struct {
   int32_t B, H, N, d;
@@ -147,6 +154,42 @@ int32_t mxattn_forward_kv_tile(int32_t d, int32_t causal);
 mxattn_status mxattn_rotate_quantize(const void* x, int32_t dtype, mxattn_shape shape,
                                      const int64_t* strides, int32_t axis, int32_t rotate,
                                      int32_t rule, mxattn_mx_tensor* out, hipStream_t stream);
+
+/* mxattn_rotate_quantize with the ceiling rule e = ceil(log2(M / q_max))
+ * (Eq. 13) for a boundary q_max in [MXATTN_Q_MIN, MXATTN_Q_MAX]
+ * (MXATTN_ERR_ENUM otherwise, or if it is not finite).  The comparison
+ * M <= q_max 2^e is exact: q_max is taken as a binary64 number.  Same
+ * layouts, arguments and padding as mxattn_rotate_quantize; out->rule is set
+ * to MXATTN_SCALE_CEIL_Q.  q_max = 7.25 reproduces the UOS codes bit for bit. */
+mxattn_status mxattn_rotate_quantize_q(const void* x, int32_t dtype, mxattn_shape shape,
+                                       const int64_t* strides, int32_t axis, int32_t rotate,
+                                       double q_max, mxattn_mx_tensor* out, hipStream_t stream);
+
+/* Workspace needed by mxattn_scale_sweep for `shape`, `axis` and n_q
+ * boundaries.  0 for an invalid shape, axis or count. */
+size_t mxattn_scale_sweep_workspace_bytes(mxattn_shape shape, int32_t axis, int32_t n_q);
+
+/* The Q_max sweep of Sec. 5.5.1 (Table 4): for every head (b, h) and every
+ * boundary q_j, the sum over the head's MXFP4 blocks of sum_i (x_i - x^_i)^2,
+ * where x is exactly what mxattn_rotate_quantize sees (the decoded input,
+ * Hadamard-rotated in binary32 if `rotate`) and x^ its MXFP4 reconstruction
+ * under e = ceil(log2(M / q_j)).  Divided by the element count of a head it
+ * is the tensor MSE the page's per-block optimum minimizes over q.
+ *   x, dtype, shape, strides, axis, rotate   as in mxattn_rotate_quantize
+ *   q_values  host array of n_q boundaries, 1 <= n_q <= MXATTN_SWEEP_MAX,
+ *             each in [MXATTN_Q_MIN, MXATTN_Q_MAX], with max <= 2 min (so a
+ *             block has at most two candidate exponents); any order
+ *   sse       device double [B*H][n_q] (head-major)
+ *   workspace device buffer of at least
+ *             mxattn_scale_sweep_workspace_bytes(shape, axis, n_q) bytes
+ * Errors: MXATTN_ERR_ENUM for a bad boundary list, MXATTN_ERR_WORKSPACE for
+ * a missing or short workspace.  The sums are accumulated in binary64 in a
+ * fixed order: the result is identical on every run, and two boundaries that
+ * select the same exponent for every block give bit-identical sums. */
+mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shape,
+                                 const int64_t* strides, int32_t axis, int32_t rotate,
+                                 const double* q_values, int32_t n_q, double* sse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Fused MXFP4 attention forward with PNQ (Alg. 2 steps 8-22).
  *   q        head-dimension MXFP4 tensor, shape [B, H, Nq, d]

@@ -21,15 +21,19 @@ LIB_PATH = os.path.join(_HERE, "libmxattn.so")
 OK = 0
 BF16, FP16 = 0, 1
 AXIS_HEAD_DIM, AXIS_TOKEN = 0, 1
-SCALE_UOS, SCALE_OCP = 0, 1
+SCALE_UOS, SCALE_OCP, SCALE_CEIL_Q = 0, 1, 2
 P_PNQ, P_DIRECT, P_POSTNORM = 0, 1, 2
 TOKEN_ALIGN = 128
+SWEEP_MAX = 48
 
 EXPORTED = (
     "mxattn_mx_codes_bytes",
     "mxattn_mx_scales_bytes",
     "mxattn_forward_kv_tile",
     "mxattn_rotate_quantize",
+    "mxattn_rotate_quantize_q",
+    "mxattn_scale_sweep_workspace_bytes",
+    "mxattn_scale_sweep",
     "mxattn_forward",
     "mxattn_reference_modes_workspace_bytes",
     "mxattn_quantize_reference_modes",
@@ -75,6 +79,13 @@ def lib():
     L.mxattn_rotate_quantize.restype = i32
     L.mxattn_rotate_quantize.argtypes = [vp, i32, Shape, vp, i32, i32, i32,
                                          ctypes.POINTER(MXTensorDesc), vp]
+    L.mxattn_rotate_quantize_q.restype = i32
+    L.mxattn_rotate_quantize_q.argtypes = [vp, i32, Shape, vp, i32, i32, ctypes.c_double,
+                                           ctypes.POINTER(MXTensorDesc), vp]
+    L.mxattn_scale_sweep_workspace_bytes.restype = sz
+    L.mxattn_scale_sweep_workspace_bytes.argtypes = [Shape, i32, i32]
+    L.mxattn_scale_sweep.restype = i32
+    L.mxattn_scale_sweep.argtypes = [vp, i32, Shape, vp, i32, i32, vp, i32, vp, vp, sz, vp]
     L.mxattn_forward.restype = i32
     L.mxattn_forward.argtypes = [ctypes.POINTER(MXTensorDesc)] * 3 + [i32, vp, vp, vp]
     L.mxattn_reference_modes_workspace_bytes.restype = sz
@@ -174,6 +185,43 @@ def rotate_quantize(x: torch.Tensor, axis: int = AXIS_HEAD_DIM, rotate: bool = T
                                         _strides(x), axis, int(bool(rotate)), rule, ctypes.byref(desc),
                                         _stream(stream)), "mxattn_rotate_quantize")
     out.shape, out.axis, out.rule, out.rotated = (B, H, N, d), axis, rule, int(bool(rotate))
+    return out
+
+
+def rotate_quantize_q(x: torch.Tensor, q_max: float, axis: int = AXIS_HEAD_DIM, rotate: bool = True,
+                      out: MXTensor | None = None, stream=None) -> MXTensor:
+    """mxattn_rotate_quantize_q: the ceiling rule e = ceil(log2(M / q_max))."""
+    B, H, N, d = x.shape
+    if out is None:
+        out = MXTensor.empty(B, H, N, d, axis, device=x.device)
+    desc = out.desc()
+    _check(lib().mxattn_rotate_quantize_q(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d),
+                                          _strides(x), axis, int(bool(rotate)), float(q_max), ctypes.byref(desc),
+                                          _stream(stream)), "mxattn_rotate_quantize_q")
+    out.shape, out.axis, out.rule, out.rotated = (B, H, N, d), axis, SCALE_CEIL_Q, int(bool(rotate))
+    return out
+
+
+def scale_sweep_workspace_bytes(B, H, N, d, axis, n_q) -> int:
+    return lib().mxattn_scale_sweep_workspace_bytes(_shape(B, H, N, d), axis, int(n_q))
+
+
+def scale_sweep(x: torch.Tensor, q_values, axis: int = AXIS_HEAD_DIM, rotate: bool = True,
+                out: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                stream=None) -> torch.Tensor:
+    """mxattn_scale_sweep: per-head sum of squared quantization errors for each
+    boundary; returns float64 [B*H, len(q_values)] on the device."""
+    B, H, N, d = x.shape
+    qs = (ctypes.c_double * len(q_values))(*[float(q) for q in q_values])
+    if out is None:
+        out = torch.empty((B * H, len(q_values)), dtype=torch.float64, device=x.device)
+    need = scale_sweep_workspace_bytes(B, H, N, d, axis, len(q_values))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _check(lib().mxattn_scale_sweep(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d), _strides(x),
+                                    axis, int(bool(rotate)), qs, len(q_values), ctypes.c_void_p(out.data_ptr()),
+                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)),
+           "mxattn_scale_sweep")
     return out
 
 

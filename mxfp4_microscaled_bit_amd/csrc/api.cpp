@@ -4,11 +4,15 @@
 #include "mxattn.h"
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "internal.h"
 
 using namespace mxattn_internal;
+
+static_assert(kSweepMax == MXATTN_SWEEP_MAX, "sweep capacity of the kernels and the header");
 
 namespace {
 
@@ -62,6 +66,52 @@ size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 mxattn_status hip_status(hipError_t e) { return e == hipSuccess ? MXATTN_OK : MXATTN_ERR_HIP; }
 
+// a ceiling-rule boundary: finite, in [MXATTN_Q_MIN, MXATTN_Q_MAX]
+bool boundary_ok(double q) { return isfinite(q) && q >= MXATTN_Q_MIN && q <= MXATTN_Q_MAX; }
+
+// binary32 bits of the largest binary32 number <= q: for a binary32 M,
+// M <= q 2^e holds exactly when it holds with this number in place of q
+uint32_t boundary_bits(double q) {
+  float f = (float)q;
+  if ((double)f > q) f = nextafterf(f, 0.0f);
+  uint32_t b;
+  memcpy(&b, &f, sizeof b);
+  return b;
+}
+
+mxattn_status quantize_common(const void* x, int32_t dtype, mxattn_shape shape, const int64_t* strides,
+                              int32_t axis, int32_t rotate, int32_t rule, uint32_t qbits,
+                              mxattn_mx_tensor* out, hipStream_t stream) {
+  if (!x || !out || !out->codes || !out->scales) return MXATTN_ERR_NULL;
+  if (dtype != MXATTN_BF16 && dtype != MXATTN_FP16) return MXATTN_ERR_DTYPE;
+  if (axis != MXATTN_AXIS_HEAD_DIM && axis != MXATTN_AXIS_TOKEN) return MXATTN_ERR_ENUM;
+  if (rotate != 0 && rotate != 1) return MXATTN_ERR_ENUM;
+  if (rotate && axis != MXATTN_AXIS_HEAD_DIM) return MXATTN_ERR_ENUM;
+  mxattn_status st = check_shape(shape);
+  if (st != MXATTN_OK) return st;
+  int64_t s[3];
+  st = resolve_strides(shape, strides, s);
+  if (st != MXATTN_OK) return st;
+  if (!aligned16(x) || !aligned16(out->codes) || !aligned16(out->scales)) return MXATTN_ERR_ALIGN;
+
+  QuantArgs a;
+  a.x = x;
+  a.dtype = dtype;
+  a.B = shape.B; a.H = shape.H; a.N = shape.N; a.d = shape.d;
+  a.sB = s[0]; a.sH = s[1]; a.sN = s[2];
+  a.rotate = rotate;
+  a.rule = rule;
+  a.qbits = qbits;
+  a.codes = out->codes;
+  a.scales = out->scales;
+  out->shape = shape;
+  out->axis = axis;
+  out->rule = rule;
+  out->rotated = rotate;
+  return hip_status(axis == MXATTN_AXIS_HEAD_DIM ? launch_quantize_headdim(a, stream)
+                                                 : launch_quantize_tokens(a, stream));
+}
+
 mxattn_status check_mx(const mxattn_mx_tensor* t, int axis) {
   if (!t || !t->codes || !t->scales) return MXATTN_ERR_NULL;
   if (t->axis != axis) return MXATTN_ERR_MISMATCH;
@@ -93,34 +143,66 @@ int32_t mxattn_forward_kv_tile(int32_t d, int32_t causal) {
 mxattn_status mxattn_rotate_quantize(const void* x, int32_t dtype, mxattn_shape shape,
                                      const int64_t* strides, int32_t axis, int32_t rotate,
                                      int32_t rule, mxattn_mx_tensor* out, hipStream_t stream) {
-  if (!x || !out || !out->codes || !out->scales) return MXATTN_ERR_NULL;
+  if (x && out && out->codes && out->scales && dtype >= 0 && dtype <= 1 &&
+      rule != MXATTN_SCALE_UOS && rule != MXATTN_SCALE_OCP)
+    return MXATTN_ERR_ENUM;
+  return quantize_common(x, dtype, shape, strides, axis, rotate, rule, 0u, out, stream);
+}
+
+mxattn_status mxattn_rotate_quantize_q(const void* x, int32_t dtype, mxattn_shape shape,
+                                       const int64_t* strides, int32_t axis, int32_t rotate,
+                                       double q_max, mxattn_mx_tensor* out, hipStream_t stream) {
+  if (x && out && out->codes && out->scales && dtype >= 0 && dtype <= 1 && !boundary_ok(q_max))
+    return MXATTN_ERR_ENUM;
+  return quantize_common(x, dtype, shape, strides, axis, rotate, MXATTN_SCALE_CEIL_Q, boundary_bits(q_max), out,
+                         stream);
+}
+
+size_t mxattn_scale_sweep_workspace_bytes(mxattn_shape shape, int32_t axis, int32_t n_q) {
+  if (check_shape(shape) != MXATTN_OK || (axis != MXATTN_AXIS_HEAD_DIM && axis != MXATTN_AXIS_TOKEN)) return 0;
+  if (n_q < 1 || n_q > MXATTN_SWEEP_MAX) return 0;
+  return round256((size_t)shape.B * shape.H * sweep_chunks(axis, shape.N, shape.d) * n_q * sizeof(double));
+}
+
+mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shape,
+                                 const int64_t* strides, int32_t axis, int32_t rotate,
+                                 const double* q_values, int32_t n_q, double* sse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!x || !q_values || !sse) return MXATTN_ERR_NULL;
   if (dtype != MXATTN_BF16 && dtype != MXATTN_FP16) return MXATTN_ERR_DTYPE;
   if (axis != MXATTN_AXIS_HEAD_DIM && axis != MXATTN_AXIS_TOKEN) return MXATTN_ERR_ENUM;
-  if (rule != MXATTN_SCALE_UOS && rule != MXATTN_SCALE_OCP) return MXATTN_ERR_ENUM;
-  if (rotate != 0 && rotate != 1) return MXATTN_ERR_ENUM;
-  if (rotate && axis != MXATTN_AXIS_HEAD_DIM) return MXATTN_ERR_ENUM;
+  if ((rotate != 0 && rotate != 1) || (rotate && axis != MXATTN_AXIS_HEAD_DIM)) return MXATTN_ERR_ENUM;
+  if (n_q < 1 || n_q > MXATTN_SWEEP_MAX) return MXATTN_ERR_ENUM;
+  double qmin = q_values[0], qmax = q_values[0];
+  for (int j = 0; j < n_q; ++j) {
+    if (!boundary_ok(q_values[j])) return MXATTN_ERR_ENUM;
+    qmin = q_values[j] < qmin ? q_values[j] : qmin;
+    qmax = q_values[j] > qmax ? q_values[j] : qmax;
+  }
+  if (qmax > 2.0 * qmin) return MXATTN_ERR_ENUM;
   mxattn_status st = check_shape(shape);
   if (st != MXATTN_OK) return st;
   int64_t s[3];
   st = resolve_strides(shape, strides, s);
   if (st != MXATTN_OK) return st;
-  if (!aligned16(x) || !aligned16(out->codes) || !aligned16(out->scales)) return MXATTN_ERR_ALIGN;
+  const size_t need = mxattn_scale_sweep_workspace_bytes(shape, axis, n_q);
+  if (!workspace || workspace_bytes < need) return MXATTN_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(sse) || !aligned16(workspace)) return MXATTN_ERR_ALIGN;
 
-  QuantArgs a;
+  SweepArgs a;
   a.x = x;
   a.dtype = dtype;
   a.B = shape.B; a.H = shape.H; a.N = shape.N; a.d = shape.d;
   a.sB = s[0]; a.sH = s[1]; a.sN = s[2];
+  a.axis = axis;
   a.rotate = rotate;
-  a.rule = rule;
-  a.codes = out->codes;
-  a.scales = out->scales;
-  out->shape = shape;
-  out->axis = axis;
-  out->rule = rule;
-  out->rotated = rotate;
-  return hip_status(axis == MXATTN_AXIS_HEAD_DIM ? launch_quantize_headdim(a, stream)
-                                                 : launch_quantize_tokens(a, stream));
+  a.nq = n_q;
+  for (int j = 0; j < n_q; ++j) a.qbits[j] = boundary_bits(q_values[j]);
+  a.qmin_bits = boundary_bits(qmin);
+  a.chunks = sweep_chunks(axis, shape.N, shape.d);
+  a.partial = static_cast<double*>(workspace);
+  a.sse = sse;
+  return hip_status(launch_scale_sweep(a, stream));
 }
 
 mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* k,

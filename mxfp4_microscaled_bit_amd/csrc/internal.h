@@ -18,13 +18,34 @@ struct QuantArgs {
   int B, H, N, d;
   int64_t sB, sH, sN;  // element strides
   int rotate;
-  int rule;  // 0 UOS, 1 OCP
+  int rule;        // 0 UOS, 1 OCP, 2 ceiling rule with boundary qbits
+  uint32_t qbits;  // rule 2: binary32 bits of the boundary q rounded down
   uint8_t* codes;
   uint8_t* scales;
 };
 
 hipError_t launch_quantize_headdim(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_tokens(const QuantArgs& a, hipStream_t stream);
+
+constexpr int kSweepMax = 48;  // boundaries per sweep call
+
+struct SweepArgs {
+  const void* x;
+  int dtype;
+  int B, H, N, d;
+  int64_t sB, sH, sN;
+  int axis;    // 0 head dimension, 1 tokens
+  int rotate;  // head dimension only
+  int nq;
+  uint32_t qbits[kSweepMax];  // binary32 bits of each boundary rounded down
+  uint32_t qmin_bits;         // the smallest boundary (largest exponent)
+  int chunks;                 // workgroups per head, sweep_chunks()
+  double* partial;            // workspace [B*H][chunks][nq]
+  double* sse;                // [B*H][nq]
+};
+
+int sweep_chunks(int axis, int N, int d);
+hipError_t launch_scale_sweep(const SweepArgs& a, hipStream_t stream);
 
 enum AttnMode : int {
   kModePnq = 0,

@@ -8,15 +8,21 @@
 //     tokens of one channel per block (Alg. 2 step 7, with the block axis that
 //     the PV product contracts over, as the MatX leaky-quantization page
 //     explains).
+//   k_sweep_headdim / k_sweep_tokens + k_sweep_reduce: the per-head squared
+//     quantization error of the same blocks for a list of ceiling-rule
+//     boundaries q (the Q_max sweep of Sec. 5.5.1, Table 4; Eq. 13).
 //
-// Both kernels are HBM-bandwidth bound: 2 bytes read and 0.5 + 1/32 bytes
-// written per element.
+// The two quantizers are HBM-bandwidth bound: 2 bytes read and 0.5 + 1/32
+// bytes written per element.  The sweep reads 2 bytes per element and does
+// two block quantizations plus one selection per boundary per block.
 //
 // Numerics follow the bit-exact contract of include/mxattn.h:
 //   rotation: binary32 butterflies with strides 1, 2, ..., d/2, then one
 //             multiply by fl32(1/sqrt(d));
-//   scale:    UOS e = ceil(log2(M / 7.25)), OCP e = floor(log2 M) - 2, read
-//             off the binary32 bit pattern of M; clamped to [-127, 127];
+//   scale:    UOS e = ceil(log2(M / 7.25)), OCP e = floor(log2 M) - 2, or the
+//             ceiling rule e = ceil(log2(M / q)) for a boundary q in [2, 64],
+//             read off the binary32 bit patterns of M (and of q rounded down
+//             to binary32); clamped to [-127, 127];
 //   elements: round to nearest E2M1 value, ties to the even code, saturating
 //             at 6, sign bit kept for values that round to zero.
 #include <hip/hip_runtime.h>
@@ -29,6 +35,7 @@ namespace {
 
 constexpr int kRuleUos = 0;
 constexpr int kRuleOcp = 1;
+constexpr int kRuleCeilQ = 2;
 
 // Two packed 16-bit inputs -> two binary32 values (exact).
 template <int DTYPE>
@@ -54,17 +61,27 @@ __device__ __forceinline__ float quad_xor2(float v) {
 // binary32 fields of M = 1.f * 2^(E-127):
 //   OCP: floor(log2 M) - 2 = E - 129;
 //   UOS: ceil(log2(M / 7.25)) = E - 129 + [1.f > 29/16]  (29/16 = 1.1101b,
-//        whose fraction field is 0x680000).
-// A zero block gets 0 (scale 1); a subnormal M needs e <= -129, which the
-// E8M0 range clamps to -127.
+//        whose fraction field is 0x680000);
+//   ceiling rule with boundary q = 1.g * 2^(Q-127) (bits `qb`):
+//        ceil(log2(M / q)) = E - Q + [1.f > 1.g].  M <= q 2^e holds for a
+//        binary32 M exactly when it holds for q rounded down to binary32, so
+//        the caller passes that rounding.
+// A zero block gets 0 (scale 1); a subnormal M needs e <= -127 for every
+// boundary >= 2, which the E8M0 range clamps to -127.
 template <int RULE>
-__device__ __forceinline__ int scale_exponent(float M) {
+__device__ __forceinline__ int scale_exponent(float M, uint32_t qb = 0u) {
   const uint32_t b = __float_as_uint(M);
   if (b == 0u) return 0;
   const int E = (int)(b >> 23);
   if (E == 0) return -127;
-  int e = E - 129;
-  if constexpr (RULE == kRuleUos) e += ((b & 0x7FFFFFu) > 0x680000u) ? 1 : 0;
+  int e;
+  if constexpr (RULE == kRuleCeilQ) {
+    e = E - (int)(qb >> 23) + (((b & 0x7FFFFFu) > (qb & 0x7FFFFFu)) ? 1 : 0);
+    e = e > 127 ? 127 : e;
+  } else {
+    e = E - 129;
+    if constexpr (RULE == kRuleUos) e += ((b & 0x7FFFFFu) > 0x680000u) ? 1 : 0;
+  }
   return e < -127 ? -127 : e;
 }
 
@@ -99,6 +116,71 @@ __device__ __forceinline__ uint4 block_codes(float* y, int e) {
   return make_uint4(cvt8(y, sc), cvt8(y + 8, sc), cvt8(y + 16, sc), cvt8(y + 24, sc));
 }
 
+template <int DTYPE>
+__device__ __forceinline__ void unpack_block(const uint4 (&raw)[4], float (&v)[32]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    unpack2<DTYPE>(raw[k].x, v[8 * k + 0], v[8 * k + 1]);
+    unpack2<DTYPE>(raw[k].y, v[8 * k + 2], v[8 * k + 3]);
+    unpack2<DTYPE>(raw[k].z, v[8 * k + 4], v[8 * k + 5]);
+    unpack2<DTYPE>(raw[k].w, v[8 * k + 6], v[8 * k + 7]);
+  }
+}
+
+// Unnormalized Hadamard butterflies of one row, for the 32-channel block
+// `blk` held by this lane; the row's d/32 blocks sit in consecutive lanes of
+// one quad.  Strides 1..16 stay in registers; stride 32 pairs this lane with
+// lane^1 and stride 64 with lane^2: the lane holding the first element keeps
+// a + b, the other b_partner - own, written as partner + (-own) with the sign
+// flipped by XOR.  Every lane of the quad must execute this.
+template <int D>
+__device__ __forceinline__ void rotate_block(float (&v)[32], int blk) {
+#pragma unroll
+  for (int hs = 1; hs < 32; hs <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      if ((i & hs) == 0) {
+        const float a = v[i], bb = v[i + hs];
+        v[i] = a + bb;
+        v[i + hs] = a - bb;
+      }
+    }
+  }
+  {
+    const uint32_t flip = (blk & 1) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float p = quad_xor1(v[i]);
+      v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+    }
+  }
+  if constexpr (D == 128) {
+    const uint32_t flip = (blk & 2) ? 0x80000000u : 0u;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const float p = quad_xor2(v[i]);
+      v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ flip);
+    }
+  }
+}
+
+// Block max of what the quantizer sees, and those values in v: with the
+// rotation, y_i = fl(v_i r) for r = fl32(1/sqrt(d)); fl32 rounding is
+// monotone, so the max of fl(|v_i| r) is fl(max|v_i| r).
+template <int D, bool ROTATE>
+__device__ __forceinline__ float finish_block(float (&v)[32]) {
+  constexpr float kRotScale = (D == 128) ? 0x1.6a09e6p-4f : 0x1p-3f;  // fl32(1/sqrt(d))
+  float mraw = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) mraw = fmaxf(mraw, fabsf(v[i]));
+  if constexpr (ROTATE) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] *= kRotScale;
+    return mraw * kRotScale;
+  }
+  return mraw;
+}
+
 // One lane owns one 32-channel block of one row (d/32 lanes per row, in the
 // same quad), so the first five butterfly stages stay in registers and the
 // remaining one (d=64) or two (d=128) cross lanes through DPP.  Each thread
@@ -107,9 +189,8 @@ __device__ __forceinline__ uint4 block_codes(float* y, int e) {
 template <int D, int DTYPE, bool ROTATE, int RULE>
 __global__ __launch_bounds__(256) void k_quantize_headdim(
     const uint16_t* __restrict__ x, int H, int N, int Np, int64_t sB, int64_t sH, int64_t sN,
-    int64_t total_units, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    int64_t total_units, uint32_t qb, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   constexpr int BPR = D / 32;  // blocks (lanes) per row
-  constexpr float kRotScale = (D == 128) ? 0x1.6a09e6p-4f : 0x1p-3f;  // fl32(1/sqrt(d))
   static_assert(D == 64 || D == 128, "head dim");
 
   uint4 raw[2][4];
@@ -136,59 +217,11 @@ __global__ __launch_bounds__(256) void k_quantize_headdim(
   for (int it = 0; it < 2; ++it) {
     const int blk = (int)(unit[it] % BPR);
     float v[32];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      unpack2<DTYPE>(raw[it][k].x, v[8 * k + 0], v[8 * k + 1]);
-      unpack2<DTYPE>(raw[it][k].y, v[8 * k + 2], v[8 * k + 3]);
-      unpack2<DTYPE>(raw[it][k].z, v[8 * k + 4], v[8 * k + 5]);
-      unpack2<DTYPE>(raw[it][k].w, v[8 * k + 6], v[8 * k + 7]);
-    }
-    if constexpr (ROTATE) {
-      // butterflies of stride 1, 2, 4, 8, 16 inside the lane
-#pragma unroll
-      for (int hs = 1; hs < 32; hs <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          if ((i & hs) == 0) {
-            const float a = v[i], bb = v[i + hs];
-            v[i] = a + bb;
-            v[i + hs] = a - bb;
-          }
-        }
-      }
-      // stride 32 pairs this lane with lane^1, stride 64 with lane^2: the lane
-      // holding the first element keeps a + b, the other b_partner - own,
-      // written as partner + (-own) with the sign flipped by XOR.
-      {
-        const uint32_t flip = (blk & 1) ? 0x80000000u : 0u;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float p = quad_xor1(v[i]);
-          v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ flip);
-        }
-      }
-      if constexpr (D == 128) {
-        const uint32_t flip = (blk & 2) ? 0x80000000u : 0u;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-          const float p = quad_xor2(v[i]);
-          v[i] = p + __uint_as_float(__float_as_uint(v[i]) ^ flip);
-        }
-      }
-    }
-    // block max of the (rotated) values; fl32 rounding is monotone, so the
-    // max of fl(|v_i| r) is fl(max|v_i| r)
-    float mraw = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) mraw = fmaxf(mraw, fabsf(v[i]));
-    const float M = ROTATE ? mraw * kRotScale : mraw;
-    const int e = scale_exponent<RULE>(M);
-
-    // y_i = fl(v_i r), then the exact division by 2^e inside the convert
-    if constexpr (ROTATE) {
-#pragma unroll
-      for (int i = 0; i < 32; ++i) v[i] *= kRotScale;
-    }
+    unpack_block<DTYPE>(raw[it], v);
+    if constexpr (ROTATE) rotate_block<D>(v, blk);
+    const float M = finish_block<D, ROTATE>(v);
+    const int e = scale_exponent<RULE>(M, qb);
+    // the exact division by 2^e happens inside the convert
     const uint4 packed = block_codes(v, e);
     if (unit[it] < total_units) {
       reinterpret_cast<uint4*>(codes)[unit[it]] = packed;
@@ -204,7 +237,7 @@ __global__ __launch_bounds__(256) void k_quantize_headdim(
 template <int D, int DTYPE, int RULE>
 __global__ __launch_bounds__(256) void k_quantize_tokens(
     const uint16_t* __restrict__ x, int H, int N, int NBp, int64_t sB, int64_t sH, int64_t sN,
-    int64_t total_blocks, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    int64_t total_blocks, uint32_t qb, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   constexpr int LPB = D / 2;  // lanes per token block
   const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t gblk = gl / LPB;
@@ -242,12 +275,205 @@ __global__ __launch_bounds__(256) void k_quantize_tokens(
     m0 = fmaxf(m0, fabsf(v0[t]));
     m1 = fmaxf(m1, fabsf(v1[t]));
   }
-  const int e0 = scale_exponent<RULE>(m0), e1 = scale_exponent<RULE>(m1);
+  const int e0 = scale_exponent<RULE>(m0, qb), e1 = scale_exponent<RULE>(m1, qb);
   uint4* dst = reinterpret_cast<uint4*>(codes + (gblk * D + 2 * cp) * 16);
   dst[0] = block_codes(v0, e0);
   dst[1] = block_codes(v1, e1);
   *reinterpret_cast<uint16_t*>(scales + gblk * D + 2 * cp) =
       (uint16_t)((uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8));
+}
+
+// ---------------------------------------------------------------------------
+// Q_max sweep (Sec. 5.5.1, Table 4): per head and per boundary q_j, the sum of
+// squared errors of the ceiling rule e = ceil(log2(M / q_j)) (Eq. 13) over the
+// blocks the quantizers above see.  With max q <= 2 min q every block has at
+// most two candidate exponents, e(q_min) and one less, so each block is
+// quantized twice and every boundary only selects one of the two errors.
+
+constexpr int kSweepUnits = 4;  // work units per lane and workgroup pass
+
+struct SweepQ {
+  uint32_t qb[kSweepMax];  // binary32 bits of each boundary, rounded down
+  uint32_t qmin;           // the smallest of them
+  int nq;
+};
+
+// the two E2M1 values in byte BYTE of w (elements 2 BYTE and 2 BYTE + 1)
+template <int BYTE>
+__device__ __forceinline__ void decode2(uint32_t w, float& lo, float& hi) {
+  const auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, BYTE);
+  lo = p[0];
+  hi = p[1];
+}
+
+__device__ __forceinline__ double pow2d(int k) { return __longlong_as_double((long long)(1023 + k) << 52); }
+
+// 4^e * sum_i (v_i 2^-e - c_i)^2 in binary64, elements in order, where c_i
+// are the E2M1 values of the block's codes at exponent e.  Every step is exact
+// except the rounding of each square and each sum: the same per-block value
+// as the plain sum of (v_i - c_i 2^e)^2.
+__device__ __forceinline__ double block_sse(const float (&v)[32], int e) {
+  float y[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) y[i] = v[i];
+  const uint4 c = block_codes(y, e);
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  float g[32];  // E2M1 values of the codes (unit scale: exact)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    decode2<0>(w[k], g[8 * k + 0], g[8 * k + 1]);
+    decode2<1>(w[k], g[8 * k + 2], g[8 * k + 3]);
+    decode2<2>(w[k], g[8 * k + 4], g[8 * k + 5]);
+    decode2<3>(w[k], g[8 * k + 6], g[8 * k + 7]);
+  }
+  const double inv = pow2d(-e);
+  double s = 0.0;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const double r = __dsub_rn(__dmul_rn((double)v[i], inv), (double)g[i]);
+    s = __dadd_rn(s, __dmul_rn(r, r));
+  }
+  return __dmul_rn(s, pow2d(2 * e));
+}
+
+__device__ __forceinline__ void accumulate_block(const float (&v)[32], float M, const SweepQ& sq,
+                                                 double (&acc)[kSweepMax]) {
+  const int e_hi = scale_exponent<kRuleCeilQ>(M, sq.qmin);
+  const int e_lo = e_hi > -127 ? e_hi - 1 : e_hi;
+  const double s_hi = block_sse(v, e_hi);
+  const double s_lo = block_sse(v, e_lo);
+#pragma unroll
+  for (int j = 0; j < kSweepMax; ++j)
+    if (j < sq.nq) acc[j] = __dadd_rn(acc[j], scale_exponent<kRuleCeilQ>(M, sq.qb[j]) == e_hi ? s_hi : s_lo);
+}
+
+// Workgroup sums of acc[j] in a fixed order (xor butterfly in each wave, then
+// the four waves in order): bit-identical on every run.
+__device__ __forceinline__ void store_partial(double (&acc)[kSweepMax], int nq, double* __restrict__ out) {
+  __shared__ double red[4][kSweepMax];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < kSweepMax; ++j) {
+    if (j < nq) {
+      double s = acc[j];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) s = __dadd_rn(s, __shfl_xor(s, o));
+      if (lane == 0) red[wave][j] = s;
+    }
+  }
+  __syncthreads();
+  if ((int)threadIdx.x < nq) {
+    const int j = threadIdx.x;
+    out[j] = __dadd_rn(__dadd_rn(__dadd_rn(red[0][j], red[1][j]), red[2][j]), red[3][j]);
+  }
+}
+
+// Head-dimension blocks, lanes mapped as in k_quantize_headdim (a row's d/32
+// blocks in one quad, so the rotation's DPP steps pair the right lanes).
+// Workgroup g covers blocks [1024 c, 1024 c + 1024) of head g / chunks,
+// c = g % chunks; blocks past the head's N rows are zeros and add nothing.
+template <int D, int DTYPE, bool ROTATE>
+__global__ __launch_bounds__(256) void k_sweep_headdim(const uint16_t* __restrict__ x, int H, int N, int64_t sB,
+                                                       int64_t sH, int64_t sN, int chunks, SweepQ sq,
+                                                       double* __restrict__ partial) {
+  constexpr int BPR = D / 32;
+  const int64_t bh = blockIdx.x / chunks;
+  const int chunk = (int)(blockIdx.x % chunks);
+  const int64_t b = bh / H, h = bh % H;
+  const int64_t units = (int64_t)N * BPR;
+  const uint16_t* xh = x + b * sB + h * sH;
+  double acc[kSweepMax];
+#pragma unroll
+  for (int j = 0; j < kSweepMax; ++j) acc[j] = 0.0;
+  for (int i = 0; i < kSweepUnits; ++i) {
+    const int64_t u = (int64_t)chunk * (256 * kSweepUnits) + i * 256 + threadIdx.x;
+    const int blk = (int)(u % BPR);
+    uint4 raw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) raw[k] = make_uint4(0, 0, 0, 0);
+    if (u < units) {
+      const uint4* p = reinterpret_cast<const uint4*>(xh + (u / BPR) * sN + 32 * blk);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) raw[k] = p[k];
+    }
+    float v[32];
+    unpack_block<DTYPE>(raw, v);
+    if constexpr (ROTATE) rotate_block<D>(v, blk);
+    const float M = finish_block<D, ROTATE>(v);
+    accumulate_block(v, M, sq, acc);
+  }
+  store_partial(acc, sq.nq, partial + blockIdx.x * (int64_t)sq.nq);
+}
+
+// Token blocks: a lane owns two adjacent channels of one 32-token block, as in
+// k_quantize_tokens; tokens past N are +0.
+template <int D, int DTYPE>
+__global__ __launch_bounds__(256) void k_sweep_tokens(const uint16_t* __restrict__ x, int H, int N, int64_t sB,
+                                                      int64_t sH, int64_t sN, int chunks, SweepQ sq,
+                                                      double* __restrict__ partial) {
+  constexpr int LPB = D / 2;
+  const int64_t bh = blockIdx.x / chunks;
+  const int chunk = (int)(blockIdx.x % chunks);
+  const int64_t b = bh / H, h = bh % H;
+  const int NB = (N + 31) / 32;
+  const int64_t units = (int64_t)NB * LPB;
+  double acc[kSweepMax];
+#pragma unroll
+  for (int j = 0; j < kSweepMax; ++j) acc[j] = 0.0;
+  for (int i = 0; i < kSweepUnits; ++i) {
+    const int64_t u = (int64_t)chunk * (256 * kSweepUnits) + i * 256 + threadIdx.x;
+    float v0[32], v1[32];
+    const int kb = (int)(u / LPB), cp = (int)(u % LPB);
+    const uint16_t* base = x + b * sB + h * sH + (int64_t)(32 * kb) * sN + 2 * cp;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const uint32_t w = (u < units && 32 * kb + t < N) ? *reinterpret_cast<const uint32_t*>(base + t * sN) : 0u;
+      unpack2<DTYPE>(w, v0[t], v1[t]);
+    }
+    float m0 = 0.0f, m1 = 0.0f;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      m0 = fmaxf(m0, fabsf(v0[t]));
+      m1 = fmaxf(m1, fabsf(v1[t]));
+    }
+    accumulate_block(v0, m0, sq, acc);
+    accumulate_block(v1, m1, sq, acc);
+  }
+  store_partial(acc, sq.nq, partial + blockIdx.x * (int64_t)sq.nq);
+}
+
+// sse[bh][j] = sum over the head's chunks, in chunk order
+__global__ __launch_bounds__(256) void k_sweep_reduce(const double* __restrict__ partial, int chunks, int nq,
+                                                      int64_t n_out, double* __restrict__ sse) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_out) return;
+  const int64_t bh = t / nq;
+  const int j = (int)(t % nq);
+  const double* p = partial + bh * chunks * (int64_t)nq + j;
+  double s = 0.0;
+  for (int c = 0; c < chunks; ++c) s = __dadd_rn(s, p[(int64_t)c * nq]);
+  sse[t] = s;
+}
+
+template <int D, int DTYPE>
+hipError_t launch_sweep_typed(const SweepArgs& a, const SweepQ& sq, hipStream_t s) {
+  const int64_t groups = (int64_t)a.B * a.H * a.chunks;
+  const uint16_t* x = static_cast<const uint16_t*>(a.x);
+  if (a.axis == 1)
+    hipLaunchKernelGGL((k_sweep_tokens<D, DTYPE>), dim3((unsigned)groups), dim3(256), 0, s, x, a.H, a.N, a.sB, a.sH,
+                       a.sN, a.chunks, sq, a.partial);
+  else if (a.rotate)
+    hipLaunchKernelGGL((k_sweep_headdim<D, DTYPE, true>), dim3((unsigned)groups), dim3(256), 0, s, x, a.H, a.N,
+                       a.sB, a.sH, a.sN, a.chunks, sq, a.partial);
+  else
+    hipLaunchKernelGGL((k_sweep_headdim<D, DTYPE, false>), dim3((unsigned)groups), dim3(256), 0, s, x, a.H, a.N,
+                       a.sB, a.sH, a.sN, a.chunks, sq, a.partial);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t n_out = (int64_t)a.B * a.H * a.nq;
+  hipLaunchKernelGGL(k_sweep_reduce, dim3((unsigned)((n_out + 255) / 256)), dim3(256), 0, s, a.partial, a.chunks,
+                     a.nq, n_out, a.sse);
+  return hipGetLastError();
 }
 
 template <int D, int DTYPE, bool ROTATE, int RULE>
@@ -257,7 +483,7 @@ hipError_t launch_hd(const QuantArgs& a, hipStream_t stream) {
   const int64_t grid = (total + 511) / 512;
   hipLaunchKernelGGL((k_quantize_headdim<D, DTYPE, ROTATE, RULE>), dim3((unsigned)grid), dim3(256), 0,
                      stream, static_cast<const uint16_t*>(a.x), a.H, a.N, (int)Np, a.sB, a.sH, a.sN,
-                     total, a.codes, a.scales);
+                     total, a.qbits, a.codes, a.scales);
   return hipGetLastError();
 }
 
@@ -269,21 +495,27 @@ hipError_t launch_tok(const QuantArgs& a, hipStream_t stream) {
   const int64_t grid = (lanes + 255) / 256;
   hipLaunchKernelGGL((k_quantize_tokens<D, DTYPE, RULE>), dim3((unsigned)grid), dim3(256), 0, stream,
                      static_cast<const uint16_t*>(a.x), a.H, a.N, (int)NBp, a.sB, a.sH, a.sN,
-                     total_blocks, a.codes, a.scales);
+                     total_blocks, a.qbits, a.codes, a.scales);
   return hipGetLastError();
+}
+
+template <int D, int DTYPE, bool ROTATE>
+hipError_t dispatch_hd_rot(const QuantArgs& a, hipStream_t s) {
+  if (a.rule == kRuleOcp) return launch_hd<D, DTYPE, ROTATE, kRuleOcp>(a, s);
+  if (a.rule == kRuleCeilQ) return launch_hd<D, DTYPE, ROTATE, kRuleCeilQ>(a, s);
+  return launch_hd<D, DTYPE, ROTATE, kRuleUos>(a, s);
 }
 
 template <int D, int DTYPE>
 hipError_t dispatch_hd_rule(const QuantArgs& a, hipStream_t s) {
-  if (a.rotate) return a.rule == kRuleOcp ? launch_hd<D, DTYPE, true, kRuleOcp>(a, s)
-                                          : launch_hd<D, DTYPE, true, kRuleUos>(a, s);
-  return a.rule == kRuleOcp ? launch_hd<D, DTYPE, false, kRuleOcp>(a, s)
-                            : launch_hd<D, DTYPE, false, kRuleUos>(a, s);
+  return a.rotate ? dispatch_hd_rot<D, DTYPE, true>(a, s) : dispatch_hd_rot<D, DTYPE, false>(a, s);
 }
 
 template <int D, int DTYPE>
 hipError_t dispatch_tok_rule(const QuantArgs& a, hipStream_t s) {
-  return a.rule == kRuleOcp ? launch_tok<D, DTYPE, kRuleOcp>(a, s) : launch_tok<D, DTYPE, kRuleUos>(a, s);
+  if (a.rule == kRuleOcp) return launch_tok<D, DTYPE, kRuleOcp>(a, s);
+  if (a.rule == kRuleCeilQ) return launch_tok<D, DTYPE, kRuleCeilQ>(a, s);
+  return launch_tok<D, DTYPE, kRuleUos>(a, s);
 }
 
 }  // namespace
@@ -296,6 +528,20 @@ hipError_t launch_quantize_headdim(const QuantArgs& a, hipStream_t stream) {
 hipError_t launch_quantize_tokens(const QuantArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.dtype == 1 ? dispatch_tok_rule<128, 1>(a, stream) : dispatch_tok_rule<128, 0>(a, stream);
   return a.dtype == 1 ? dispatch_tok_rule<64, 1>(a, stream) : dispatch_tok_rule<64, 0>(a, stream);
+}
+
+int sweep_chunks(int axis, int N, int d) {
+  const int64_t units = axis == 1 ? (int64_t)((N + 31) / 32) * (d / 2) : (int64_t)N * (d / 32);
+  return (int)((units + 256 * kSweepUnits - 1) / (256 * kSweepUnits));
+}
+
+hipError_t launch_scale_sweep(const SweepArgs& a, hipStream_t stream) {
+  SweepQ sq;
+  for (int j = 0; j < kSweepMax; ++j) sq.qb[j] = j < a.nq ? a.qbits[j] : 0u;
+  sq.qmin = a.qmin_bits;
+  sq.nq = a.nq;
+  if (a.d == 128) return a.dtype == 1 ? launch_sweep_typed<128, 1>(a, sq, stream) : launch_sweep_typed<128, 0>(a, sq, stream);
+  return a.dtype == 1 ? launch_sweep_typed<64, 1>(a, sq, stream) : launch_sweep_typed<64, 0>(a, sq, stream);
 }
 
 }  // namespace mxattn_internal

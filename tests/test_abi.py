@@ -136,3 +136,39 @@ def test_reference_modes_reject_bad_arguments():
     assert ref(ws_bytes=need - 1) == 7
     assert ref(q=FAKE + 2) == 4
     assert ref(sums=FAKE + 12) == 4
+
+
+def test_ceiling_rule_and_sweep_reject_bad_arguments():
+    L = mx.lib()
+    out = mx.MXTensorDesc(FAKE, FAKE + 4096, mx.Shape(0, 0, 0, 0), 5, 5, 5)
+    shp = mx.Shape(1, 1, 64, 64)
+
+    def rq(q=7.0, x=FAKE, axis=0, rotate=1, dtype=0):
+        return L.mxattn_rotate_quantize_q(x, dtype, shp, None, axis, rotate, q, ctypes.byref(out), None)
+
+    assert rq(x=None) == 1
+    assert rq(dtype=4) == 3
+    for q in (1.99, 64.5, float("nan"), float("inf"), -7.0):
+        assert rq(q=q) == 8
+    assert rq(axis=1, rotate=1) == 8
+    assert (out.axis, out.rule, out.rotated) == (5, 5, 5)  # untouched on error
+    # the plain entry point does not take the ceiling rule (it needs q)
+    assert L.mxattn_rotate_quantize(FAKE, 0, shp, None, 0, 1, mx.SCALE_CEIL_Q, ctypes.byref(out), None) == 8
+
+    need = mx.scale_sweep_workspace_bytes(1, 1, 64, 64, mx.AXIS_HEAD_DIM, 3)
+    assert need > 0 and mx.scale_sweep_workspace_bytes(1, 1, 64, 64, mx.AXIS_HEAD_DIM, 49) == 0
+    assert mx.scale_sweep_workspace_bytes(1, 1, 64, 64, 3, 1) == 0
+
+    def sw(qs=(6.0, 7.0, 8.0), x=FAKE, sse=FAKE, ws=FAKE, ws_bytes=None, axis=0, rotate=1):
+        arr = (ctypes.c_double * max(len(qs), 1))(*qs)
+        return L.mxattn_scale_sweep(x, 0, shp, None, axis, rotate, arr, len(qs), sse, ws,
+                                    need if ws_bytes is None else ws_bytes, None)
+
+    assert sw(x=None) == 1 and sw(sse=None) == 1
+    assert sw(qs=()) == 8
+    assert sw(qs=tuple([7.0] * 49)) == 8
+    assert sw(qs=(6.0, 12.5)) == 8          # max > 2 min
+    assert sw(qs=(1.5, 2.5)) == 8           # below the range
+    assert sw(axis=1, rotate=1) == 8
+    assert sw(ws=None) == 7 and sw(ws_bytes=need - 1) == 7
+    assert sw(sse=FAKE + 8) == 4
