@@ -56,6 +56,10 @@ def _load():
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_double,
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
+    lib.oracle_p_diagnostics.restype = ctypes.c_int
+    lib.oracle_p_diagnostics.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                         ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_void_p,
+                                         ctypes.c_void_p]
     lib.oracle_scale_sweep.restype = ctypes.c_int
     lib.oracle_scale_sweep.argtypes = [
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -215,6 +219,29 @@ def scale_sweep(x_bits, dtype, B, H, N, d, qs, *, axis=AXIS_HEAD_DIM, rotate=Fal
     if rc != 0:
         raise ValueError("oracle_scale_sweep rejected its arguments")
     return sse
+
+
+def p_diagnostics(q_bits, k_bits, dtype, B, H, N, d, *, causal=False, rotate=True, rule=RULE_UOS,
+                  gamma=1.0, rows=None, strides=None, amb_delta=0.0, nthreads=None):
+    """Row-sum diagnostics of materialized-P quantization (see oracle.h).
+    Returns (diag float64 [B,H,R,6], amb float64 [B,H,R])."""
+    for a in (q_bits, k_bits):
+        assert np.asarray(a).dtype == np.uint16
+    rows_a = None if rows is None else np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+    R = N if rows_a is None else rows_a.size
+    cfg = AttnCfg(B, H, N, d, dtype, int(bool(causal)), int(bool(rotate)), 1, rule, P_POSTNORM, 128,
+                  nthreads or default_threads(), 0.0, float(amb_delta), 0)
+    diag = np.empty((B, H, R, 6), np.float64)
+    amb = np.empty((B, H, R), np.float64)
+    st = _strides(strides)
+    qa, ka = np.asarray(q_bits), np.asarray(k_bits)
+    if st is None:
+        qa, ka = np.ascontiguousarray(qa), np.ascontiguousarray(ka)
+    rc = _load().oracle_p_diagnostics(ctypes.byref(cfg), _ptr(qa), _ptr(ka), _ptr(st), _ptr(rows_a), R,
+                                      float(gamma), _ptr(diag), _ptr(amb))
+    if rc != 0:
+        raise ValueError("oracle_p_diagnostics rejected its arguments")
+    return diag, amb
 
 
 def attention(q_bits, k_bits, v_bits, dtype, B, H, N, d, *, causal=False, rotate=True,

@@ -463,11 +463,11 @@ static void load_query(const attn_ctx* c, int64_t b, int64_t h, int i, double* q
  * an element lying near a rounding midpoint may round to the neighbouring
  * grid point, and a block maximum lying near a scale boundary may select the
  * neighbouring exponent (the whole block is then re-projected). */
-static void quantize_p_block(const oracle_attn_cfg* g, const double* p, double* ph, double* dp) {
+static int quantize_p_block(const oracle_attn_cfg* g, const double* p, double* ph, double* dp) {
   uint8_t codes[32], sb;
   int e = oracle_quantize_block(p, 32, g->rule, g->q, &sb, codes);
   for (int t = 0; t < 32; ++t) ph[t] = dequant(codes[t], sb);
-  if (!dp) return;
+  if (!dp) return e;
   const double delta = g->amb_delta;
   for (int t = 0; t < 32; ++t) {
     dp[t] = 0.0;
@@ -483,7 +483,7 @@ static void quantize_p_block(const oracle_attn_cfg* g, const double* p, double* 
   double M = 0.0;
   for (int t = 0; t < 32; ++t)
     if (p[t] > M) M = p[t];
-  if (M <= 0.0) return;
+  if (M <= 0.0) return e;
   /* normalized block max and the two ends of its admissible interval */
   double r = ldexp(M, -e), hi, lo;
   switch (g->rule) {
@@ -503,6 +503,7 @@ static void quantize_p_block(const oracle_attn_cfg* g, const double* p, double* 
       if (diff > dp[t]) dp[t] = diff;
     }
   }
+  return e;
 }
 
 static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
@@ -709,4 +710,117 @@ int oracle_attention(const oracle_attn_cfg* cfg,
                                      3 * (size_t)T + 32) +
                    sizeof(float) * d + 64;
   return run_pool(attn_item, &c, heads * cph, scratch, nth);
+}
+
+/* ------------------------------------------------------------------ */
+/* materialized-P row-sum diagnostics                                   */
+
+typedef struct {
+  const oracle_attn_cfg* cfg;
+  const uint16_t *q, *k;
+  int64_t sB, sH, sN;
+  const int32_t* rows;
+  int32_t n_rows;
+  int32_t chunks_per_head, rows_per_chunk;
+  double gamma;
+  double *diag, *amb;
+} diag_ctx;
+
+/* One chunk of rows of one head [P1 Sec. 5.5.2, Fig. 7]: the exact softmax
+ * row P_i. = exp(S_i. - m) / l over the visible keys, then P^ = Q(gamma P) /
+ * gamma with the block quantizer on aligned 32-key blocks (a pre-quantization
+ * global scale gamma, 1 for the plain diagnostic, Fig. 7 (C)).  The row-sum
+ * error sum_j (P^ - P) is split by the outcome of each element: zeroing
+ * (P > 0, P^ = 0), saturation (gamma P / 2^e beyond the largest grid value
+ * 6), and otherwise downward (P^ < P) or upward (P^ > P) rounding; plus the
+ * row's entropy -sum P ln P (nats, Fig. 7 (D)). */
+static void diag_item(void* vctx, int64_t item, void* scratch_raw) {
+  const diag_ctx* c = (const diag_ctx*)vctx;
+  const oracle_attn_cfg* g = c->cfg;
+  const int N = g->N, d = g->d;
+  const int64_t bh = item / c->chunks_per_head;
+  const int chunk = (int)(item % c->chunks_per_head);
+  const int64_t b = bh / g->H, h = bh % g->H;
+  int r0 = chunk * c->rows_per_chunk, r1 = r0 + c->rows_per_chunk;
+  if (r1 > c->n_rows) r1 = c->n_rows;
+  if (r0 >= r1) return;
+  char* s = (char*)scratch_raw;
+  double* K = (double*)s;  s += sizeof(double) * (size_t)N * d;
+  double* V = (double*)s;  s += sizeof(double) * (size_t)N * d;
+  double* qv = (double*)s; s += sizeof(double) * d;
+  double* sc = (double*)s; s += sizeof(double) * (size_t)N;
+  double* blk = (double*)s; s += sizeof(double) * 32;
+  float* buf = (float*)s;  s += sizeof(float) * d;
+  uint8_t* codes = (uint8_t*)s;
+  attn_ctx ac;
+  memset(&ac, 0, sizeof ac);
+  ac.cfg = g; ac.q = c->q; ac.k = c->k; ac.v = c->k;
+  ac.sB = c->sB; ac.sH = c->sH; ac.sN = c->sN;
+  ac.kB = c->sB; ac.kH = c->sH; ac.kN = c->sN; ac.Nk = N;
+  load_head_kv(&ac, b, h, K, V, buf, codes, blk);
+  const double inv_sqrt_d = 1.0 / sqrt((double)d);
+  for (int r = r0; r < r1; ++r) {
+    const int i = c->rows ? c->rows[r] : r;
+    load_query(&ac, b, h, i, qv, buf, codes, blk);
+    const int jvis = g->causal ? (i + 1 < N ? i + 1 : N) : N;
+    double ms = -INFINITY, ls = 0.0;
+    for (int j = 0; j < jvis; ++j) {
+      double acc = 0.0;
+      for (int t = 0; t < d; ++t) acc += qv[t] * K[(int64_t)j * d + t];
+      sc[j] = acc * inv_sqrt_d;
+      if (sc[j] > ms) ms = sc[j];
+    }
+    for (int j = 0; j < jvis; ++j) ls += exp(sc[j] - ms);
+    double out[6] = {0, 0, 0, 0, 0, 0}, amb = 0.0;
+    for (int j0 = 0; j0 < jvis; j0 += 32) {
+      double P[32], gp[32], hb[32], db[32];
+      for (int t = 0; t < 32; ++t) {
+        P[t] = (j0 + t < jvis) ? exp(sc[j0 + t] - ms) / ls : 0.0;
+        gp[t] = c->gamma * P[t];
+      }
+      const int e = quantize_p_block(g, gp, hb, c->amb ? db : NULL);
+      for (int t = 0; t < 32 && j0 + t < jvis; ++t) {
+        const double ph = hb[t] / c->gamma, diff = ph - P[t];
+        out[0] += ph;
+        if (P[t] > 0.0 && ph == 0.0) out[1] += diff;
+        else if (ldexp(gp[t], -e) > 6.0) out[2] += diff;
+        else if (diff < 0.0) out[3] += diff;
+        else if (diff > 0.0) out[4] += diff;
+        if (P[t] > 0.0) out[5] -= P[t] * log(P[t]);
+        if (c->amb) amb += db[t] / c->gamma;
+      }
+    }
+    const int64_t ridx = bh * c->n_rows + r;
+    for (int k = 0; k < 6; ++k) c->diag[ridx * 6 + k] = out[k];
+    if (c->amb) c->amb[ridx] = amb;
+  }
+}
+
+int oracle_p_diagnostics(const oracle_attn_cfg* cfg, const uint16_t* q, const uint16_t* k,
+                         const int64_t* strides, const int32_t* rows, int32_t n_rows, double gamma,
+                         double* diag, double* amb) {
+  if (!cfg || !q || !k || !diag) return -1;
+  if (!shape_ok(cfg->B, cfg->H, cfg->N, cfg->d)) return -1;
+  if (!(gamma > 0.0) || !isfinite(gamma) || !cfg->quant) return -1;
+  if (cfg->rule != ORACLE_RULE_UOS && cfg->rule != ORACLE_RULE_OCP) return -1;
+  if (!rows) n_rows = cfg->N;
+  if (n_rows < 1) return -1;
+  if (rows)
+    for (int r = 0; r < n_rows; ++r)
+      if (rows[r] < 0 || rows[r] >= cfg->N) return -1;
+  diag_ctx c;
+  memset(&c, 0, sizeof c);
+  c.cfg = cfg; c.q = q; c.k = k;
+  strides_or_contig(strides, cfg->H, cfg->N, cfg->d, &c.sB, &c.sH, &c.sN);
+  c.rows = rows; c.n_rows = n_rows; c.gamma = gamma; c.diag = diag; c.amb = amb;
+  const int64_t heads = (int64_t)cfg->B * cfg->H;
+  int nth = cfg->nthreads > 0 ? cfg->nthreads : 1;
+  int cph = (int)((2 * (int64_t)nth + heads - 1) / heads);
+  if (cph < 1) cph = 1;
+  if (cph > n_rows) cph = n_rows;
+  c.chunks_per_head = cph;
+  c.rows_per_chunk = (n_rows + cph - 1) / cph;
+  const int N = cfg->N, d = cfg->d;
+  size_t scratch = sizeof(double) * ((size_t)2 * N * d + d + N + 32) + sizeof(float) * d + 64;
+  return run_pool(diag_item, &c, heads * cph, scratch, nth);
 }

@@ -163,6 +163,25 @@ int oracle_attention(const oracle_attn_cfg* cfg,
                      double* out, double* m_out, double* l_out, double* rowsum,
                      double* amb, double* absmass);
 
+/* Row-sum diagnostics of quantizing the materialized probabilities
+ * [P1 Sec. 5.5.2, Fig. 7]: for each listed query row (rows / n_rows as in
+ * oracle_attention; cfg->rule UOS or OCP, cfg->quant = 1, cfg->kv_tile
+ * ignored), P = softmax(S) over the visible keys exactly, P^ = Q(gamma P) /
+ * gamma with aligned 32-key blocks.  diag [B][H][n_rows][6]:
+ *   0  sum_j P^_ij                     (the induced row sum)
+ *   1  zeroing: sum of P^ - P over elements with P > 0, P^ = 0
+ *   2  saturation: over elements with gamma P / 2^e > 6
+ *   3  downward rounding: over the remaining elements with P^ < P
+ *   4  upward rounding: over elements with P^ > P
+ *   5  entropy -sum_j P_ij ln P_ij (nats)
+ * so that diag[0] - 1 = diag[1] + diag[2] + diag[3] + diag[4].
+ * amb [B][H][n_rows] (nullable): sum over the row of the largest change of
+ * P^_ij that a decision within relative margin cfg->amb_delta of a
+ * threshold could make.  Returns 0, or -1 on a bad argument. */
+int oracle_p_diagnostics(const oracle_attn_cfg* cfg, const uint16_t* q, const uint16_t* k,
+                         const int64_t* strides, const int32_t* rows, int32_t n_rows, double gamma,
+                         double* diag, double* amb);
+
 #ifdef __cplusplus
 }
 #endif

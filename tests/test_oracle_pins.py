@@ -767,3 +767,60 @@ def test_sweep_head_selection_and_arguments():
         qs = bad.pop("qs")
         with pytest.raises(ValueError):
             oracle.scale_sweep(x, W.BF16, B, H, N, d, qs, **bad)
+
+
+# --------------------------------------------------------------------------
+# materialized-P row-sum diagnostics  [P1 Sec. 5.5.2, Fig. 7]
+
+
+def test_diagnostics_uniform_row_closed_form():
+    """Q = 0 makes every score 0, so P = 1/N on every row.  For N = 100 the UOS
+    block scale is 2^ceil(log2(0.01/7.25)) = 2^-9, 0.01 * 2^9 = 5.12 rounds up
+    to 6, and every element becomes 6/512: row sum 1.171875, all of it upward
+    rounding, entropy ln 100.  A pre-quantization scale gamma = 1.25 moves the
+    normalized value to 6.4, beyond the grid: every element saturates to 6,
+    P^ = 6/512/1.25 and the row sum is 0.9375.  OCP picks the same scale here."""
+    B, H, N, d = 1, 1, 100, 64
+    x = W.custom(B, H, N, d, seed=40)
+    zq = np.zeros_like(x["q"])
+    for rule in (oracle.RULE_UOS, oracle.RULE_OCP):
+        diag, _ = oracle.p_diagnostics(zq, x["k"], W.BF16, B, H, N, d, rule=rule)
+        assert np.allclose(diag[..., 0], 1.171875, rtol=0, atol=1e-12)
+        assert np.allclose(diag[..., 4], 0.171875, rtol=0, atol=1e-12)
+        assert np.all(diag[..., 1:4] == 0)
+        assert np.allclose(diag[..., 5], math.log(100), rtol=0, atol=1e-12)
+    diag, _ = oracle.p_diagnostics(zq, x["k"], W.BF16, B, H, N, d, gamma=1.25)
+    assert np.allclose(diag[..., 0], 0.9375, rtol=0, atol=1e-12)
+    assert np.allclose(diag[..., 2], -0.0625, rtol=0, atol=1e-12)
+    assert np.all(diag[..., [1, 3, 4]] == 0)
+    # causal: row i sees i + 1 equal keys; row 0 holds P = 1, which UOS maps to
+    # the grid value 4 at scale 1/4 exactly
+    diag, _ = oracle.p_diagnostics(zq, x["k"], W.BF16, B, H, N, d, causal=True)
+    assert diag[0, 0, 0, 0] == 1.0 and diag[0, 0, 0, 5] == 0.0
+    assert np.allclose(diag[0, 0, 99], [1.171875, 0, 0, 0, 0.171875, math.log(100)], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cid", [1, 5])
+def test_diagnostics_decomposition_and_postnorm_row_sums(cid):
+    """The four outcome classes partition the elements, so their contributions
+    add up to the row-sum error; the row sum equals the POSTNORM forward's
+    induced row sum; a power-of-two gamma changes nothing (the E8M0 scale
+    absorbs it)."""
+    w = W.WORKLOADS[cid]
+    B, H, N, d = w.shape
+    heads = [(0, 0), (0, 1)]
+    sel = {t: W.generate(w, t, heads=heads)[None] for t in "qkv"}
+    rows = np.arange(0, N, max(1, N // 97), dtype=np.int32)
+    diag, _ = oracle.p_diagnostics(sel["q"], sel["k"], w.dtype, 1, 2, N, d, rows=rows)
+    parts = diag[..., 1:5].sum(axis=-1)
+    assert np.abs(diag[..., 0] - 1 - parts).max() < 1e-12
+    assert (diag[..., 1] <= 0).all() and (diag[..., 2] <= 0).all() and (diag[..., 3] <= 0).all()
+    assert (diag[..., 4] >= 0).all()
+    assert (diag[..., 5] >= 0).all() and (diag[..., 5] <= math.log(N) + 1e-9).all()
+    ref = oracle.attention(sel["q"], sel["k"], sel["v"], w.dtype, 1, 2, N, d, p_mode=oracle.P_POSTNORM, rows=rows)
+    assert np.abs(diag[..., 0] - ref["rowsum"]).max() < 1e-12
+    d4, _ = oracle.p_diagnostics(sel["q"], sel["k"], w.dtype, 1, 2, N, d, rows=rows, gamma=4.0)
+    assert np.abs(d4[..., :5] - diag[..., :5]).max() < 1e-15
+    # the sharp workload zeroes many elements; the outlier one saturates some
+    if cid == 5:
+        assert diag[..., 1].min() < -1e-3
