@@ -239,6 +239,44 @@ mxattn_status mxattn_quantize_reference_modes(const void* q, const void* k, cons
                                               float* out, float* row_sums, void* workspace,
                                               size_t workspace_bytes, hipStream_t stream);
 
+/* Workspace needed by mxattn_p_diagnostics for `shape` (Q^, K^ and the
+ * per-row statistics).  0 for an invalid shape. */
+size_t mxattn_p_diagnostics_workspace_bytes(mxattn_shape shape);
+
+/* Row-sum diagnostics of quantizing the materialized probabilities
+ * (Sec. 5.5.2, Fig. 7), from 16-bit Q and K: quantize Q and K with `rule`
+ * (rotating them if `rotate`), compute the exact softmax P = softmax(S) of
+ * every row (a first pass finds m and l), and quantize gamma P in aligned
+ * 32-key blocks with `rule`: P^ = Q(gamma P) / gamma.  gamma is the
+ * pre-quantization global scale of Fig. 7 (C); 1 gives the plain
+ * diagnostic.  Writes, per query row, 6 floats:
+ *   diag[.., 0]  sum_j P^_ij, the induced row sum (Fig. 7 (A));
+ *   diag[.., 1..4]  the row-sum error sum_j (P^_ij - P_ij) split by the
+ *                outcome of each element (Fig. 7 (B)): zeroing (P > 0 but
+ *                P^ = 0), saturation (gamma P / 2^e above the largest E2M1
+ *                value 6), downward and upward rounding of the rest;
+ *   diag[.., 5]  the row's entropy -sum_j P_ij ln P_ij in nats (Fig. 7 (D)).
+ * No value tensor and no PV product are involved.
+ *   q, k, dtype, shape, strides   as in mxattn_quantize_reference_modes
+ *   rule      MXATTN_SCALE_UOS or MXATTN_SCALE_OCP (Q, K and P)
+ *   causal    1: key j is visible to query i iff j <= i
+ *   gamma     in [2^-20, 2^20]
+ *   diag      device float [B, H, N, 6], contiguous
+ *   workspace device buffer of at least
+ *             mxattn_p_diagnostics_workspace_bytes(shape) bytes
+ * P is evaluated in binary32 (exp2 of (s - m) c - log2 l); sums accumulate
+ * in binary32.  gamma enters only through gamma_f in gamma = 2^k gamma_f,
+ * 1 <= gamma_f < 2: a power-of-two factor moves every block exponent by k
+ * and cancels, so such gammas give bit-identical results.  Errors:
+ * MXATTN_ERR_NULL, MXATTN_ERR_DTYPE, MXATTN_ERR_ENUM (rule, rotate, causal,
+ * gamma outside its range or NaN), the shape and stride errors of
+ * mxattn_rotate_quantize, MXATTN_ERR_WORKSPACE, MXATTN_ERR_ALIGN (a pointer
+ * not 16-byte aligned); nothing is enqueued on an error. */
+mxattn_status mxattn_p_diagnostics(const void* q, const void* k, int32_t dtype, mxattn_shape shape,
+                                   const int64_t* strides, int32_t rule, int32_t rotate, int32_t causal,
+                                   float gamma, float* diag, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* mxattn_status_string(mxattn_status status);
 

@@ -37,6 +37,8 @@ EXPORTED = (
     "mxattn_forward",
     "mxattn_reference_modes_workspace_bytes",
     "mxattn_quantize_reference_modes",
+    "mxattn_p_diagnostics_workspace_bytes",
+    "mxattn_p_diagnostics",
     "mxattn_status_string",
 )
 
@@ -93,6 +95,10 @@ def lib():
     L.mxattn_quantize_reference_modes.restype = i32
     L.mxattn_quantize_reference_modes.argtypes = [vp, vp, vp, i32, Shape, vp, i32, i32, i32, i32,
                                                   vp, vp, vp, sz, vp]
+    L.mxattn_p_diagnostics_workspace_bytes.restype = sz
+    L.mxattn_p_diagnostics_workspace_bytes.argtypes = [Shape]
+    L.mxattn_p_diagnostics.restype = i32
+    L.mxattn_p_diagnostics.argtypes = [vp, vp, i32, Shape, vp, i32, i32, i32, ctypes.c_float, vp, vp, sz, vp]
     L.mxattn_status_string.restype = ctypes.c_char_p
     L.mxattn_status_string.argtypes = [i32]
     _lib = L
@@ -266,6 +272,30 @@ def quantize_reference_modes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
         ctypes.c_void_p(out.data_ptr()), None if row_sums is None else ctypes.c_void_p(row_sums.data_ptr()),
         ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)),
         "mxattn_quantize_reference_modes")
+    return out
+
+
+def p_diagnostics_workspace_bytes(B, H, N, d) -> int:
+    return lib().mxattn_p_diagnostics_workspace_bytes(_shape(B, H, N, d))
+
+
+def p_diagnostics(q: torch.Tensor, k: torch.Tensor, rule: int = SCALE_UOS, rotate: bool = True,
+                  causal: bool = False, gamma: float = 1.0, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mxattn_p_diagnostics; returns float32 [B, H, N, 6]: row sum, zeroing,
+    saturation, downward, upward rounding contributions, entropy (nats)."""
+    if q.shape != k.shape or q.dtype != k.dtype or q.stride() != k.stride():
+        raise ValueError("q and k must share shape, dtype and strides")
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, 6), dtype=torch.float32, device=q.device)
+    need = p_diagnostics_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib().mxattn_p_diagnostics(
+        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), _dtype_enum(q), _shape(B, H, N, d), _strides(q),
+        rule, int(bool(rotate)), int(bool(causal)), float(gamma), ctypes.c_void_p(out.data_ptr()),
+        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)), "mxattn_p_diagnostics")
     return out
 
 

@@ -237,6 +237,8 @@ mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* 
   a.row_stats = row_stats;
   a.row_sums = nullptr;
   a.stats_ws = nullptr;
+  a.diag = nullptr;
+  a.gamma = 1.0f;
   return hip_status(launch_attention(a, stream));
 }
 
@@ -298,6 +300,62 @@ mxattn_status mxattn_quantize_reference_modes(const void* q, const void* k, cons
   a.row_stats = nullptr;
   a.row_sums = row_sums;
   a.stats_ws = p_mode == MXATTN_P_POSTNORM ? stats : nullptr;
+  a.diag = nullptr;
+  a.gamma = 1.0f;
+  return hip_status(launch_attention(a, stream));
+}
+
+size_t mxattn_p_diagnostics_workspace_bytes(mxattn_shape shape) {
+  if (check_shape(shape) != MXATTN_OK) return 0;
+  return 2 * (round256(codes_bytes(shape, 0)) + round256(scales_bytes(shape, 0))) +
+         round256((size_t)shape.B * shape.H * padded_tokens(shape.N) * 2 * sizeof(float));
+}
+
+mxattn_status mxattn_p_diagnostics(const void* q, const void* k, int32_t dtype, mxattn_shape shape,
+                                   const int64_t* strides, int32_t rule, int32_t rotate, int32_t causal,
+                                   float gamma, float* diag, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (!q || !k || !diag) return MXATTN_ERR_NULL;
+  if (dtype != MXATTN_BF16 && dtype != MXATTN_FP16) return MXATTN_ERR_DTYPE;
+  if (rule != MXATTN_SCALE_UOS && rule != MXATTN_SCALE_OCP) return MXATTN_ERR_ENUM;
+  if ((rotate != 0 && rotate != 1) || (causal != 0 && causal != 1)) return MXATTN_ERR_ENUM;
+  if (!(gamma >= 0x1p-20f && gamma <= 0x1p20f)) return MXATTN_ERR_ENUM;  // also rejects NaN
+  mxattn_status st = check_shape(shape);
+  if (st != MXATTN_OK) return st;
+  int64_t s[3];
+  st = resolve_strides(shape, strides, s);
+  if (st != MXATTN_OK) return st;
+  const size_t need = mxattn_p_diagnostics_workspace_bytes(shape);
+  if (!workspace || workspace_bytes < need) return MXATTN_ERR_WORKSPACE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(diag) || !aligned16(workspace)) return MXATTN_ERR_ALIGN;
+
+  uint8_t* w = static_cast<uint8_t*>(workspace);
+  const size_t cb = round256(codes_bytes(shape, 0)), sb = round256(scales_bytes(shape, 0));
+  mxattn_mx_tensor tq = {w, w + cb, shape, 0, 0, 0};
+  mxattn_mx_tensor tk = {w + cb + sb, w + 2 * cb + sb, shape, 0, 0, 0};
+  float* stats = reinterpret_cast<float*>(w + 2 * (cb + sb));
+  st = mxattn_rotate_quantize(q, dtype, shape, strides, MXATTN_AXIS_HEAD_DIM, rotate, rule, &tq, stream);
+  if (st != MXATTN_OK) return st;
+  st = mxattn_rotate_quantize(k, dtype, shape, strides, MXATTN_AXIS_HEAD_DIM, rotate, rule, &tk, stream);
+  if (st != MXATTN_OK) return st;
+
+  AttnArgs a;
+  a.qc = tq.codes; a.qs = tq.scales;
+  a.kc = tk.codes; a.ks = tk.scales;
+  // no PV product: the value tiles the kernel stages are never read, so K^
+  // (a buffer of the same size) stands in for them
+  a.vc = tk.codes; a.vs = tk.scales;
+  a.B = shape.B; a.H = shape.H; a.N = shape.N; a.d = shape.d;
+  a.Nk = shape.N;
+  a.causal = causal;
+  a.mode = kModeDiag;
+  a.rule = rule;
+  a.out = nullptr;
+  a.row_stats = nullptr;
+  a.row_sums = nullptr;
+  a.stats_ws = stats;
+  a.diag = diag;
+  a.gamma = gamma;
   return hip_status(launch_attention(a, stream));
 }
 

@@ -67,6 +67,9 @@ struct Params {
   float* row_stats;
   float* row_sums;
   float* stats;
+  float* diag;
+  float gamma_f;      // DIAG: gamma = 2^k gamma_f, gamma_f in [1, 2)
+  float inv_gamma_f;  // DIAG: 1 / gamma_f
   int H;
   int N, Np;    // keys / values: count and padded count
   int Nq, Nqp;  // queries: count and padded count
@@ -310,6 +313,8 @@ struct FwdConsts {
   // reproduce exact ties, so they evaluate fma(s - m, c, -off), which is
   // exact when s = m.
   static constexpr bool kExactArg = !(MODE == kModePnq && RULE == kRuleUos);
+  // the running maximum is fixed (exact statistics of a first pass)
+  static constexpr bool kFixedM = (MODE == kModePostnorm || MODE == kModeDiag);
   static constexpr float kC = (D == 128) ? 0x1.0527dcp-3f : 0x1.715476p-3f;  // log2(e)/sqrt(d)
   static constexpr float kInvSqrtD = (D == 128) ? 0x1.6a09e6p-4f : 0x1p-3f;  // 1/sqrt(d)
 };
@@ -362,6 +367,73 @@ __device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, 
   return make_uint4(pack_fp4x8(y), pack_fp4x8(y + 8), pack_fp4x8(y + 16), pack_fp4x8(y + 24));
 }
 
+// the two E2M1 values in byte BYTE of w (elements 2 BYTE and 2 BYTE + 1)
+template <int BYTE>
+__device__ __forceinline__ void decode_fp4x2(uint32_t w, float& lo, float& hi) {
+  const auto p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, BYTE);
+  lo = p[0];
+  hi = p[1];
+}
+
+// Row-sum diagnostics of one 32-key block of the lane's query (Sec. 5.5.2,
+// Fig. 7) for the exact softmax P = exp2(a), a = (s - m) c - off with
+// off = log2 l.  The quantizer input is gamma P.  A power-of-two factor of
+// gamma = 2^k gamma_f only moves the block exponent by k and cancels in
+// Q(gamma P) / gamma, so only gamma_f enters: the block scale 2^e comes from
+// gamma_f max(P), and y = gamma_f P / 2^e goes to the FP4 convert.  Per
+// block, in units of 2^e / gamma_f: the grid values g give the row sum
+// (sum g) and the errors g - y split by outcome -- zeroing (g = 0 < y),
+// saturation (y > 6), downward or upward rounding; the entropy term
+// P log2 P = y (a) in the same units.
+// dg: [row sum, zeroing, saturation, down, up, sum P log2 P].
+template <int D, int RULE>
+__device__ __forceinline__ void diag_block(const v16f& s0, const v16f& s1, float bmax, const RowState& rs,
+                                           float gamma_f, float inv_gamma_f, float (&dg)[6]) {
+  using F = FwdConsts<D, kModeDiag, RULE>;
+  const int e = scale_exponent<RULE>(__builtin_amdgcn_exp2f(fmaf(bmax - rs.m, F::kC, -rs.off)) * gamma_f);
+  const float nb = -(rs.off + (float)e);
+  const float fe = (float)e;
+  float gsum = 0.0f, cz = 0.0f, cs = 0.0f, cd = 0.0f, cu = 0.0f, ent = 0.0f;
+  // eight elements at a time: exponentials, codes, their values, the sums
+#pragma unroll
+  for (int c8 = 0; c8 < 4; ++c8) {
+    const v16f& src = (c8 < 2) ? s0 : s1;
+    float arg[8], y[8], gq[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      arg[k] = fmaf(src[8 * (c8 & 1) + k] - rs.m, F::kC, nb);  // log2(P / 2^e)
+      y[k] = __builtin_amdgcn_exp2f(arg[k]) * gamma_f;
+    }
+    const uint32_t w = pack_fp4x8(y);
+    decode_fp4x2<0>(w, gq[0], gq[1]);
+    decode_fp4x2<1>(w, gq[2], gq[3]);
+    decode_fp4x2<2>(w, gq[4], gq[5]);
+    decode_fp4x2<3>(w, gq[6], gq[7]);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float g = gq[k], yy = y[k];
+      const float df = g - yy;
+      const bool zero = (g == 0.0f) & (yy > 0.0f);
+      const bool sat = yy > 6.0f;
+      gsum += g;
+      cz += zero ? df : 0.0f;
+      cs += (!zero & sat) ? df : 0.0f;
+      cd += (!zero & !sat & (df < 0.0f)) ? df : 0.0f;
+      cu += (df > 0.0f) ? df : 0.0f;
+      ent += (yy > 0.0f) ? yy * (arg[k] + fe) : 0.0f;
+    }
+    __builtin_amdgcn_sched_barrier(0);  // one group of eight live at a time
+  }
+  // back from block units: P^ = g 2^e / gamma_f, P = y 2^e / gamma_f
+  const float unit = __builtin_amdgcn_ldexpf(inv_gamma_f, e);
+  dg[0] = fmaf(gsum, unit, dg[0]);
+  dg[1] = fmaf(cz, unit, dg[1]);
+  dg[2] = fmaf(cs, unit, dg[2]);
+  dg[3] = fmaf(cd, unit, dg[3]);
+  dg[4] = fmaf(cu, unit, dg[4]);
+  dg[5] = fmaf(ent, unit, dg[5]);
+}
+
 // scores of keys the query may not see -> -inf (element 4j+i of sub-tile t
 // of lane group g is key 64(t/2) + 32g + 16(t%2) + 4j + i of the tile)
 template <bool CAUSAL, bool MASKED>
@@ -397,7 +469,8 @@ __device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
 template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
 __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[D / 64],
                                           int qsc, int q, uint4 ones, int one_sc, RowState& rs, v16f (&acc)[D / 32],
-                                          v4f& accl, int (&held)[4], int lane, const int (&koff)[D / 64]) {
+                                          v4f& accl, int (&held)[4], int lane, const int (&koff)[D / 64],
+                                          float (&dg)[6], float gamma_f, float inv_gamma_f) {
   using L = Lds<D>;
   using F = FwdConsts<D, MODE, RULE>;
   constexpr int NH = D / 64;   // K steps of one S^T sub-tile
@@ -433,7 +506,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   keep_live(tmax, (int)ksw.x, (int)ksw.y, one_sc);
   keep_live(tmax, held[0], held[1], held[2], held[3]);
   float a = 1.0f;
-  if constexpr (MODE != kModePostnorm) {
+  if constexpr (!F::kFixedM) {
     const float m_new = fmaxf(rs.m, pair_max(tmax));
     if (m_new != -INFINITY) {
       a = __builtin_amdgcn_exp2f((rs.m - m_new) * F::kC);  // 0 on the first visited tile
@@ -448,6 +521,10 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
 #pragma unroll
       for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f((s[t][e] - rs.m) * F::kC);
     rs.l = a * rs.l + pair_sum(sum);
+  } else if constexpr (MODE == kModeDiag) {
+    __builtin_amdgcn_sched_barrier(0);
+    diag_block<D, RULE>(s[0], s[1], bmax[0], rs, gamma_f, inv_gamma_f, dg);
+    diag_block<D, RULE>(s[2], s[3], bmax[1], rs, gamma_f, inv_gamma_f, dg);
   } else {
     const uint2 vsw = *reinterpret_cast<const uint2*>(buf + L::VS + 8 * lane);
     if constexpr (MODE != kModePostnorm) {
@@ -537,12 +614,13 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   rs.mc = 0.0f;
   rs.off = 0.0f;
   rs.l = 0.0f;
-  if constexpr (MODE == kModePostnorm) {
+  if constexpr (F::kFixedM) {
     const float* st = p.stats + qrow * 2;
     rs.m = st[0];
     rs.off = __builtin_amdgcn_logf(st[1]);  // log2 of l*
     rs.mc = st[0] * F::kC + rs.off;
   }
+  float dg[6] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   v16f acc[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
@@ -565,7 +643,7 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
     codes_dma<D>(p, plan, bh, kn, nxt, tid);
     const ScaleRegs sr = scale_load<D>(p, bh, kn, tid);
     tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, one_sc, rs, acc, accl, held, lane,
-                                            koff);
+                                            koff, dg, p.gamma_f, p.inv_gamma_f);
     scale_store<D>(sr, nxt, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -573,7 +651,7 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   // at most one masked tile: the ragged end of the keys or the causal diagonal
   if (nfull < nkt)
     tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, ones, one_sc, rs,
-                                           acc, accl, held, lane, koff);
+                                           acc, accl, held, lane, koff, dg, p.gamma_f, p.inv_gamma_f);
 
   // ---- epilogue
   if constexpr (MODE == kModeStats) {
@@ -581,6 +659,20 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
       float* st2 = p.stats + qrow * 2;
       st2[0] = rs.m;
       st2[1] = rs.l;
+    }
+    return;
+  }
+  if constexpr (MODE == kModeDiag) {
+#pragma unroll
+    for (int k = 0; k < 6; ++k) dg[k] = pair_sum(dg[k]);
+    if (g == 0 && qi < p.Nq) {
+      float* dr = p.diag + (bh * p.Nq + qi) * 6;
+      dr[0] = dg[0];
+      dr[1] = dg[1];
+      dr[2] = dg[2];
+      dr[3] = dg[3];
+      dr[4] = dg[4];
+      dr[5] = -0x1.62e430p-1f * dg[5];  // -ln 2 * sum P log2 P
     }
     return;
   }
@@ -632,9 +724,12 @@ hipError_t dispatch_mode(const AttnArgs& a, const Params& prm, hipStream_t s) {
   if (a.mode == kModeDirect)
     return a.rule == kRuleUos ? launch_one<D, CAUSAL, kModeDirect, kRuleUos>(prm, BH, s)
                               : launch_one<D, CAUSAL, kModeDirect, kRuleOcp>(prm, BH, s);
-  // POSTNORM: exact row statistics first, then the quantized pass
+  // POSTNORM, DIAG: exact row statistics first, then the quantized pass
   hipError_t err = launch_one<D, CAUSAL, kModeStats, kRuleUos>(prm, BH, s);
   if (err != hipSuccess) return err;
+  if (a.mode == kModeDiag)
+    return a.rule == kRuleUos ? launch_one<D, CAUSAL, kModeDiag, kRuleUos>(prm, BH, s)
+                              : launch_one<D, CAUSAL, kModeDiag, kRuleOcp>(prm, BH, s);
   return a.rule == kRuleUos ? launch_one<D, CAUSAL, kModePostnorm, kRuleUos>(prm, BH, s)
                             : launch_one<D, CAUSAL, kModePostnorm, kRuleOcp>(prm, BH, s);
 }
@@ -648,6 +743,14 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
   prm.row_stats = a.row_stats;
   prm.row_sums = a.row_sums;
   prm.stats = a.stats_ws;
+  prm.diag = a.diag;
+  {
+    // gamma = 2^k gamma_f with gamma_f in [1, 2); 1/gamma_f rounds once
+    int k = 0;
+    const float gf = a.mode == kModeDiag ? 2.0f * frexpf(a.gamma, &k) : 1.0f;
+    prm.gamma_f = gf;
+    prm.inv_gamma_f = 1.0f / gf;
+  }
   prm.H = a.H;
   prm.N = a.Nk;
   prm.Np = (int)padded_tokens(a.Nk);

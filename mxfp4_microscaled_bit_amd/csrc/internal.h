@@ -51,6 +51,7 @@ enum AttnMode : int {
   kModePnq = 0,
   kModeDirect = 1,
   kModePostnorm = 2,
+  kModeDiag = 4,  // row-sum diagnostics of materialized P (no PV product)
 };
 
 struct AttnArgs {
@@ -68,7 +69,9 @@ struct AttnArgs {
   float* out;        // [B, H, N, d]
   float* row_stats;  // nullable [B, H, N, 2] (m, l)
   float* row_sums;   // nullable [B, H, N]
-  float* stats_ws;   // POSTNORM: [B, H, Np, 2] exact (m, l) of pass 1
+  float* stats_ws;   // POSTNORM, DIAG: [B, H, Np, 2] exact (m, l) of pass 1
+  float* diag;       // DIAG: [B, H, N, 6]
+  float gamma;       // DIAG: pre-quantization global scale of P
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);

@@ -172,3 +172,26 @@ def test_ceiling_rule_and_sweep_reject_bad_arguments():
     assert sw(axis=1, rotate=1) == 8
     assert sw(ws=None) == 7 and sw(ws_bytes=need - 1) == 7
     assert sw(sse=FAKE + 8) == 4
+
+
+def test_p_diagnostics_rejects_bad_arguments():
+    L = mx.lib()
+    need = mx.p_diagnostics_workspace_bytes(1, 1, 64, 64)
+    # Q^, K^ (codes + scales, 128 padded rows each) and the fp32 (m, l) pairs
+    assert need >= 2 * (128 * 32 + 128 * 2) + 128 * 2 * 4
+    assert mx.p_diagnostics_workspace_bytes(1, 1, 64, 96) == 0
+
+    def dg(q=FAKE, k=FAKE, dtype=0, shape=(1, 1, 64, 64), rule=0, rotate=1, causal=0, gamma=1.0, out=FAKE,
+           ws=FAKE, ws_bytes=None):
+        return L.mxattn_p_diagnostics(q, k, dtype, mx.Shape(*shape), None, rule, rotate, causal, gamma, out, ws,
+                                      need if ws_bytes is None else ws_bytes, None)
+
+    assert dg(q=None) == 1 and dg(k=None) == 1 and dg(out=None) == 1
+    assert dg(dtype=2) == 3
+    assert dg(rule=mx.SCALE_CEIL_Q) == 8 and dg(rule=-1) == 8
+    assert dg(rotate=2) == 8 and dg(causal=3) == 8
+    for gamma in (0.0, -1.0, float("nan"), float("inf"), 2.0 ** 21, 2.0 ** -21):
+        assert dg(gamma=gamma) == 8, gamma
+    assert dg(shape=(1, 1, 64, 32)) == 2
+    assert dg(ws=None) == 7 and dg(ws_bytes=need - 1) == 7
+    assert dg(out=FAKE + 4) == 4 and dg(k=FAKE + 2) == 4
