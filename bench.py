@@ -14,7 +14,10 @@ the dense MXFP4 matrix-core peak; its duration comes from HIP events recorded
 around each forward launch on the launch stream.  `cpu_baseline` times the
 plain CPU oracle on a bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--no-cpu-baseline]
+With --fused-q the step quantizes K and V and runs the forward entry point
+that rotates and quantizes Q in its own prologue (no Q^ buffer).
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--fused-q] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -108,6 +111,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--fused-q", action="store_true",
+                    help="rotate and quantize Q inside the forward (mxattn_forward_fused_q)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run three plain device-to-device copies of BYTES bytes and exit "
@@ -172,12 +177,16 @@ def main():
         e = [ev() for _ in range(3)] if record is not None else None
         if e:
             e[0].record(stream)
-        mx.rotate_quantize(dev["q"], mx.AXIS_HEAD_DIM, rotate=True, out=qm)
+        if not args.fused_q:
+            mx.rotate_quantize(dev["q"], mx.AXIS_HEAD_DIM, rotate=True, out=qm)
         mx.rotate_quantize(dev["k"], mx.AXIS_HEAD_DIM, rotate=True, out=km)
         mx.rotate_quantize(dev["v"], mx.AXIS_TOKEN, rotate=False, out=vm)
         if e:
             e[1].record(stream)
-        mx.forward(qm, km, vm, causal=w.causal, out=out)
+        if args.fused_q:
+            mx.forward_fused_q(dev["q"], km, vm, causal=w.causal, out=out)
+        else:
+            mx.forward(qm, km, vm, causal=w.causal, out=out)
         if e:
             e[2].record(stream)
             record.append(e)
@@ -198,7 +207,7 @@ def main():
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
-    quant_bytes = B * H * (N + 2 * Nk) * d * QUANT_BYTES_PER_ELEMENT
+    quant_bytes = B * H * ((0 if args.fused_q else N) + 2 * Nk) * d * QUANT_BYTES_PER_ELEMENT
     quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
 
     result = {
@@ -214,8 +223,11 @@ def main():
         "vs_baseline": None,
         "dtype": "fp4",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: {w.describe()}, one step = rotate+quantize Q, K; quantize V; "
-                               f"fused PNQ forward", "B": B, "H": H, "N": N, "d": d,
+        "config": {"workload": f"{w.name}: {w.describe()}, one step = " +
+                               ("rotate+quantize K; quantize V; fused PNQ forward with Q rotated and "
+                                "quantized in its prologue" if args.fused_q else
+                                "rotate+quantize Q, K; quantize V; fused PNQ forward"),
+                   "B": B, "H": H, "N": N, "d": d, "fused_q": bool(args.fused_q),
                    "causal": w.causal, "kv_tile": mx.forward_kv_tile(d, w.causal),
                    **({"Nk": Nk} if Nk != N else {})},
         "forward": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
@@ -225,7 +237,7 @@ def main():
                       "bytes": quant_bytes},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(flops) if args.workload == 2 else None},
+                     "traffic": measured_traffic(flops) if args.workload == 2 and not args.fused_q else None},
     }
     if not args.no_cpu_baseline and Nk == N and not w.causal:
         log("timing the CPU oracle on a bounded sample")

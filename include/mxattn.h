@@ -213,6 +213,26 @@ mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* 
                              const mxattn_mx_tensor* v, int32_t causal, float* out,
                              float* row_stats, hipStream_t stream);
 
+/* mxattn_forward with the Q preprocessing fused into its prologue: the
+ * paper puts the Hadamard rotation inside the Q/K preprocessing stage at
+ * negligible cost (Sec. 4.3; Alg. 2 steps 3-6).  Each workgroup rotates (if
+ * k->rotated) and quantizes its own query rows with k's rule, exactly as
+ * mxattn_rotate_quantize would (bit for bit), and keeps Q^ on chip: no Q^
+ * buffer, no separate launch.  The output equals that of
+ * mxattn_rotate_quantize + mxattn_forward bit for bit.
+ *   q, dtype   16-bit Q (MXATTN_BF16 or MXATTN_FP16), device, 16-byte aligned
+ *   q_shape    [B, H, Nq, d]
+ *   q_strides  as in mxattn_rotate_quantize (NULL: contiguous)
+ *   k, v, causal, out, row_stats   as in mxattn_forward; k->rule must be
+ *              MXATTN_SCALE_UOS or MXATTN_SCALE_OCP (else MXATTN_ERR_ENUM)
+ * Errors: those of mxattn_forward (with q_shape in place of q->shape), and
+ * MXATTN_ERR_NULL, MXATTN_ERR_DTYPE, MXATTN_ERR_SHAPE, MXATTN_ERR_STRIDE,
+ * MXATTN_ERR_ALIGN for q; nothing is enqueued on an error. */
+mxattn_status mxattn_forward_fused_q(const void* q, int32_t dtype, mxattn_shape q_shape,
+                                     const int64_t* q_strides, const mxattn_mx_tensor* k,
+                                     const mxattn_mx_tensor* v, int32_t causal, float* out,
+                                     float* row_stats, hipStream_t stream);
+
 /* Workspace needed by mxattn_quantize_reference_modes for `shape`/`p_mode`
  * (the three MXFP4 tensors, plus per-row statistics for POSTNORM).
  * 0 for an invalid shape or mode. */

@@ -35,6 +35,7 @@ EXPORTED = (
     "mxattn_scale_sweep_workspace_bytes",
     "mxattn_scale_sweep",
     "mxattn_forward",
+    "mxattn_forward_fused_q",
     "mxattn_reference_modes_workspace_bytes",
     "mxattn_quantize_reference_modes",
     "mxattn_p_diagnostics_workspace_bytes",
@@ -99,6 +100,8 @@ def lib():
     L.mxattn_p_diagnostics_workspace_bytes.argtypes = [Shape]
     L.mxattn_p_diagnostics.restype = i32
     L.mxattn_p_diagnostics.argtypes = [vp, vp, i32, Shape, vp, i32, i32, i32, ctypes.c_float, vp, vp, sz, vp]
+    L.mxattn_forward_fused_q.restype = i32
+    L.mxattn_forward_fused_q.argtypes = [vp, i32, Shape, vp, vp, vp, i32, vp, vp, vp]
     L.mxattn_status_string.restype = ctypes.c_char_p
     L.mxattn_status_string.argtypes = [i32]
     _lib = L
@@ -248,6 +251,29 @@ def forward(q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: to
                                 ctypes.c_void_p(out.data_ptr()),
                                 None if row_stats is None else ctypes.c_void_p(row_stats.data_ptr()),
                                 _stream(stream)), "mxattn_forward")
+    return out
+
+
+def forward_fused_q(q: torch.Tensor, k: MXTensor, v: MXTensor, causal: bool = False,
+                    out: torch.Tensor | None = None, row_stats: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """mxattn_forward_fused_q: Q is a 16-bit [B, H, Nq, d] tensor, rotated (if k
+    is) and quantized with k's rule inside the forward; returns O as float32
+    [B, H, Nq, d]."""
+    B, H, N, d = q.shape
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+    if out.dtype != torch.float32 or not out.is_contiguous() or tuple(out.shape) != (B, H, N, d):
+        raise ValueError("out must be a contiguous float32 [B, H, N, d] tensor")
+    if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
+                                  or row_stats.numel() != B * H * N * 2):
+        raise ValueError("row_stats must be a contiguous float32 [B, H, N, 2] tensor")
+    dk, dv = k.desc(), v.desc()
+    _check(lib().mxattn_forward_fused_q(
+        ctypes.c_void_p(q.data_ptr()), _dtype_enum(q), _shape(B, H, N, d), _strides(q), ctypes.byref(dk),
+        ctypes.byref(dv), int(bool(causal)), ctypes.c_void_p(out.data_ptr()),
+        None if row_stats is None else ctypes.c_void_p(row_stats.data_ptr()), _stream(stream)),
+        "mxattn_forward_fused_q")
     return out
 
 

@@ -121,6 +121,46 @@ mxattn_status check_mx(const mxattn_mx_tensor* t, int axis) {
   return MXATTN_OK;
 }
 
+// checks shared by the two forward entry points; q_shape / q_rotated
+// describe Q^ (or, fused, the Q it is made from)
+mxattn_status check_forward(const mxattn_shape& q_shape, int32_t q_rotated, const mxattn_mx_tensor* k,
+                            const mxattn_mx_tensor* v, int32_t causal, const float* out, const float* row_stats) {
+  if (!out) return MXATTN_ERR_NULL;
+  mxattn_status st = check_mx(k, MXATTN_AXIS_HEAD_DIM);
+  if (st != MXATTN_OK) return st;
+  st = check_mx(v, MXATTN_AXIS_TOKEN);
+  if (st != MXATTN_OK) return st;
+  // K^ and V^ share one shape; Q may have another token count
+  // (cross-attention) but the same B, H and d
+  if (!same_shape(k->shape, v->shape)) return MXATTN_ERR_MISMATCH;
+  if (q_shape.B != k->shape.B || q_shape.H != k->shape.H || q_shape.d != k->shape.d) return MXATTN_ERR_MISMATCH;
+  if ((q_rotated != 0) != (k->rotated != 0)) return MXATTN_ERR_MISMATCH;
+  if (causal != 0 && causal != 1) return MXATTN_ERR_ENUM;
+  if (causal && q_shape.N != k->shape.N) return MXATTN_ERR_MISMATCH;
+  if (!aligned16(out) || (row_stats && !aligned16(row_stats))) return MXATTN_ERR_ALIGN;
+  return MXATTN_OK;
+}
+
+AttnArgs forward_args(const mxattn_shape& q_shape, const mxattn_mx_tensor* k, const mxattn_mx_tensor* v,
+                      int32_t causal, float* out, float* row_stats) {
+  AttnArgs a;
+  a.qc = nullptr; a.qs = nullptr;
+  a.kc = k->codes; a.ks = k->scales;
+  a.vc = v->codes; a.vs = v->scales;
+  a.B = q_shape.B; a.H = q_shape.H; a.N = q_shape.N; a.d = q_shape.d;
+  a.Nk = k->shape.N;
+  a.causal = causal;
+  a.mode = kModePnq;
+  a.rule = MXATTN_SCALE_UOS;
+  a.out = out;
+  a.row_stats = row_stats;
+  a.row_sums = nullptr;
+  a.stats_ws = nullptr;
+  a.diag = nullptr;
+  a.gamma = 1.0f;
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -205,40 +245,40 @@ mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shap
   return hip_status(launch_scale_sweep(a, stream));
 }
 
+
 mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* k,
                              const mxattn_mx_tensor* v, int32_t causal, float* out,
                              float* row_stats, hipStream_t stream) {
-  if (!out) return MXATTN_ERR_NULL;
   mxattn_status st = check_mx(q, MXATTN_AXIS_HEAD_DIM);
   if (st != MXATTN_OK) return st;
-  st = check_mx(k, MXATTN_AXIS_HEAD_DIM);
+  st = check_forward(q->shape, q->rotated, k, v, causal, out, row_stats);
   if (st != MXATTN_OK) return st;
-  st = check_mx(v, MXATTN_AXIS_TOKEN);
-  if (st != MXATTN_OK) return st;
-  // K^ and V^ share one shape; Q^ may have another token count
-  // (cross-attention) but the same B, H and d
-  if (!same_shape(k->shape, v->shape)) return MXATTN_ERR_MISMATCH;
-  if (q->shape.B != k->shape.B || q->shape.H != k->shape.H || q->shape.d != k->shape.d) return MXATTN_ERR_MISMATCH;
-  if ((q->rotated != 0) != (k->rotated != 0)) return MXATTN_ERR_MISMATCH;
-  if (causal != 0 && causal != 1) return MXATTN_ERR_ENUM;
-  if (causal && q->shape.N != k->shape.N) return MXATTN_ERR_MISMATCH;
-  if (!aligned16(out) || (row_stats && !aligned16(row_stats))) return MXATTN_ERR_ALIGN;
-
-  AttnArgs a;
+  AttnArgs a = forward_args(q->shape, k, v, causal, out, row_stats);
   a.qc = q->codes; a.qs = q->scales;
-  a.kc = k->codes; a.ks = k->scales;
-  a.vc = v->codes; a.vs = v->scales;
-  a.B = q->shape.B; a.H = q->shape.H; a.N = q->shape.N; a.d = q->shape.d;
-  a.Nk = k->shape.N;
-  a.causal = causal;
-  a.mode = kModePnq;
-  a.rule = MXATTN_SCALE_UOS;
-  a.out = out;
-  a.row_stats = row_stats;
-  a.row_sums = nullptr;
-  a.stats_ws = nullptr;
-  a.diag = nullptr;
-  a.gamma = 1.0f;
+  return hip_status(launch_attention(a, stream));
+}
+
+mxattn_status mxattn_forward_fused_q(const void* q, int32_t dtype, mxattn_shape q_shape,
+                                     const int64_t* q_strides, const mxattn_mx_tensor* k,
+                                     const mxattn_mx_tensor* v, int32_t causal, float* out,
+                                     float* row_stats, hipStream_t stream) {
+  if (!q) return MXATTN_ERR_NULL;
+  if (dtype != MXATTN_BF16 && dtype != MXATTN_FP16) return MXATTN_ERR_DTYPE;
+  mxattn_status st = check_shape(q_shape);
+  if (st != MXATTN_OK) return st;
+  int64_t s[3];
+  st = resolve_strides(q_shape, q_strides, s);
+  if (st != MXATTN_OK) return st;
+  if (!aligned16(q)) return MXATTN_ERR_ALIGN;
+  if (k && k->rule != MXATTN_SCALE_UOS && k->rule != MXATTN_SCALE_OCP) return MXATTN_ERR_ENUM;
+  st = check_forward(q_shape, k ? k->rotated : 0, k, v, causal, out, row_stats);
+  if (st != MXATTN_OK) return st;
+  AttnArgs a = forward_args(q_shape, k, v, causal, out, row_stats);
+  a.qx = q;
+  a.qdtype = dtype;
+  a.qsB = s[0]; a.qsH = s[1]; a.qsN = s[2];
+  a.qrotate = k->rotated != 0;
+  a.qrule = k->rule;
   return hip_status(launch_attention(a, stream));
 }
 

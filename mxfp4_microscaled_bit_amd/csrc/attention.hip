@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include "internal.h"
+#include "mx_block.h"
 
 namespace mxattn_internal {
 namespace {
@@ -70,6 +71,11 @@ struct Params {
   float* diag;
   float gamma_f;      // DIAG: gamma = 2^k gamma_f, gamma_f in [1, 2)
   float inv_gamma_f;  // DIAG: 1 / gamma_f
+  const uint16_t* qx;        // fused Q prologue: 16-bit Q [B, H, Nq, d]
+  int64_t qsB, qsH, qsN;     // its element strides
+  int qdtype;                // 0 bf16, 1 fp16
+  int qrotate;               // Hadamard-rotate Q first
+  int qrule;                 // 0 UOS, 1 OCP
   int H;
   int N, Np;    // keys / values: count and padded count
   int Nq, Nqp;  // queries: count and padded count
@@ -84,6 +90,8 @@ struct Lds {
   static constexpr int VC = KS + 64 * 8;        // V^ codes [block][channel][16]
   static constexpr int VS = VC + 64 * D;        // V^ scales, [lane][PV step] dwords
   static constexpr int STAGE = VS + 64 * 8;
+  // the fused Q prologue parks Q^ of the workgroup's kBr rows in a stage
+  static_assert(kBr * D / 2 <= KS - KC && kBr * D / 32 <= VC - KS, "Q^ scratch exceeds a stage");
 };
 
 // key (0..127 within the tile) on A-operand row r of S^T sub-tile t
@@ -460,6 +468,58 @@ __device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
   return m;
 }
 
+// Fused Q prologue (Sec. 4.3: the rotation belongs to the Q preprocessing):
+// the wave rotates and quantizes its own 32 query rows exactly as the
+// standalone head-dimension quantizer does, with the same block device code,
+// and leaves codes and scales in the Q^ layout: rows of d/2 code bytes at
+// `codes`, rows of d/32 scale bytes at `scales`.  Lane L takes the
+// 32-channel blocks u = 64 it + L, it < d/64: row u / (d/32), block
+// u % (d/32), so each row's blocks sit in one quad, as the butterflies need.
+// Rows past the last query are zero (codes 0, scale 2^0), as in Q^'s padding.
+template <int D>
+__device__ __forceinline__ void q_prologue_load(const Params& p, int64_t bh, int row0, int lane,
+                                                uint4 (&raw)[D / 64][4]) {
+  constexpr int BPR = D / 32;
+  const int64_t b = bh / p.H, h = bh % p.H;
+#pragma unroll
+  for (int it = 0; it < D / 64; ++it) {
+    const int u = 64 * it + lane;
+    const int n = row0 + u / BPR, blk = u % BPR;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) raw[it][k] = make_uint4(0u, 0u, 0u, 0u);
+    if (n < p.Nq) {
+      const uint4* src = reinterpret_cast<const uint4*>(p.qx + b * p.qsB + h * p.qsH + (int64_t)n * p.qsN + 32 * blk);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) raw[it][k] = src[k];
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void q_prologue_quantize(const Params& p, int lane, const uint4 (&raw)[D / 64][4],
+                                                    uint8_t* codes, uint8_t* scales) {
+  constexpr int BPR = D / 32;
+#pragma unroll
+  for (int it = 0; it < D / 64; ++it) {
+    const int u = 64 * it + lane;
+    const int row = u / BPR, blk = u % BPR;
+    float v[32];
+    if (p.qdtype == 0) mxblock::unpack_block<0>(raw[it], v);
+    else mxblock::unpack_block<1>(raw[it], v);
+    float M;
+    if (p.qrotate) {
+      mxblock::rotate_block<D>(v, blk);
+      M = mxblock::finish_block<D, true>(v);
+    } else {
+      M = mxblock::finish_block<D, false>(v);
+    }
+    const int e = (p.qrule == kRuleUos) ? mxblock::scale_exponent<mxblock::kRuleUos>(M)
+                                        : mxblock::scale_exponent<mxblock::kRuleOcp>(M);
+    *reinterpret_cast<uint4*>(codes + row * (D / 2) + 16 * blk) = mxblock::block_codes(v, e);
+    scales[row * BPR + blk] = (uint8_t)(e + 127);
+  }
+}
+
 // One key tile for the wave's 32 queries.  Order: all S products; block and
 // row maxima; P^ of the first 64-key half and its PV products, which run on
 // the matrix cores while P^ of the second half is formed; then the second
@@ -503,7 +563,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   const float tmax = fmaxf(bmax[0], bmax[1]);
   // this tile's S products and the previous tile's PV products have read
   // their scales once tmax exists
-  keep_live(tmax, (int)ksw.x, (int)ksw.y, one_sc);
+  keep_live(tmax, (int)ksw.x, (int)ksw.y, one_sc, qsc);
   keep_live(tmax, held[0], held[1], held[2], held[3]);
   float a = 1.0f;
   if constexpr (!F::kFixedM) {
@@ -559,8 +619,11 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   }
 }
 
-template <int D, bool CAUSAL, int MODE, int RULE>
-__global__ __launch_bounds__(256, 2) void k_attention(Params p) {
+// Two workgroups (two waves per SIMD) per CU; the diagnostics pass keeps
+// more per-element state and runs with one, which gives it the accumulation
+// registers instead of scratch spills.
+template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ>
+__global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Params p) {
   using L = Lds<D>;
   using F = FwdConsts<D, MODE, RULE>;
   constexpr int NH = D / 64;
@@ -591,10 +654,12 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   const int64_t qrow = bh * p.Nqp + qi;
   uint4 qop[NH];
   int qsc;
+  if constexpr (!FUSEDQ) {
 #pragma unroll
-  for (int h = 0; h < NH; ++h) qop[h] = *reinterpret_cast<const uint4*>(p.qc + qrow * (D / 2) + 16 * (2 * h + g));
-  if constexpr (D == 128) qsc = (int)p.qs[qrow * 4 + g] | ((int)p.qs[qrow * 4 + 2 + g] << 8);
-  else qsc = (int)p.qs[qrow * 2 + g];
+    for (int h = 0; h < NH; ++h) qop[h] = *reinterpret_cast<const uint4*>(p.qc + qrow * (D / 2) + 16 * (2 * h + g));
+    if constexpr (D == 128) qsc = (int)p.qs[qrow * 4 + g] | ((int)p.qs[qrow * 4 + 2 + g] << 8);
+    else qsc = (int)p.qs[qrow * 2 + g];
+  }
 
   // 0/1 A operand of the l product (row L%16, K chunk L/16)
   const uint32_t onew = ((((lane & 15) >> 2) & 1) == ((lane >> 4) & 1)) ? 0x22222222u : 0u;  // E2M1 1.0
@@ -628,10 +693,33 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   v4f accl = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
   const DmaPlan<D> plan(tid);
-  codes_dma<D>(p, plan, bh, 0, lds, tid);
-  scale_store<D>(scale_load<D>(p, bh, 0, tid), lds, tid);
-  __builtin_amdgcn_s_waitcnt(0);  // the DMA has landed in LDS
-  __syncthreads();
+  if constexpr (FUSEDQ) {
+    // Q rows are loaded under the first tile's DMA, quantized into the second
+    // LDS stage (free until the loop's first copy), and read back in operand
+    // order; a second barrier frees that stage again
+    uint4 raw[D / 64][4];
+    q_prologue_load<D>(p, bh, qt * kBr + 32 * wave, lane, raw);
+    codes_dma<D>(p, plan, bh, 0, lds, tid);
+    scale_store<D>(scale_load<D>(p, bh, 0, tid), lds, tid);
+    uint8_t* qlds = lds + L::STAGE + L::KC + 32 * wave * (D / 2);  // this wave's 32 rows
+    uint8_t* qslds = lds + L::STAGE + L::KS + 32 * wave * (D / 32);
+    q_prologue_quantize<D>(p, lane, raw, qlds, qslds);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    const uint8_t* qr = qlds + r * (D / 2);
+    const uint8_t* qsr = qslds + r * (D / 32);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) qop[h] = *reinterpret_cast<const uint4*>(qr + 16 * (2 * h + g));
+    if constexpr (D == 128) qsc = (int)qsr[g] | ((int)qsr[2 + g] << 8);
+    else qsc = (int)qsr[g];
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  } else {
+    codes_dma<D>(p, plan, bh, 0, lds, tid);
+    scale_store<D>(scale_load<D>(p, bh, 0, tid), lds, tid);
+    __builtin_amdgcn_s_waitcnt(0);  // the DMA has landed in LDS
+    __syncthreads();
+  }
 
   // full tiles: no per-element masking; the next tile is copied into the
   // other buffer while this one is processed (on the last iteration the
@@ -709,16 +797,18 @@ __global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   }
 }
 
-template <int D, bool CAUSAL, int MODE, int RULE>
+template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ = false>
 hipError_t launch_one(const Params& prm, int BH, hipStream_t stream) {
   const int64_t groups = (int64_t)BH * prm.nqt;
-  hipLaunchKernelGGL((k_attention<D, CAUSAL, MODE, RULE>), dim3((unsigned)groups), dim3(256), 0, stream, prm);
+  hipLaunchKernelGGL((k_attention<D, CAUSAL, MODE, RULE, FUSEDQ>), dim3((unsigned)groups), dim3(256), 0, stream,
+                     prm);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL>
 hipError_t dispatch_mode(const AttnArgs& a, const Params& prm, hipStream_t s) {
   const int BH = a.B * a.H;
+  if (a.qx) return launch_one<D, CAUSAL, kModePnq, kRuleUos, true>(prm, BH, s);  // fused Q prologue
   if (a.mode == kModePnq && a.rule == kRuleUos) return launch_one<D, CAUSAL, kModePnq, kRuleUos>(prm, BH, s);
   if (a.mode == kModePnq) return launch_one<D, CAUSAL, kModePnq, kRuleOcp>(prm, BH, s);
   if (a.mode == kModeDirect)
@@ -751,6 +841,11 @@ hipError_t launch_attention(const AttnArgs& a, hipStream_t stream) {
     prm.gamma_f = gf;
     prm.inv_gamma_f = 1.0f / gf;
   }
+  prm.qx = static_cast<const uint16_t*>(a.qx);
+  prm.qsB = a.qsB; prm.qsH = a.qsH; prm.qsN = a.qsN;
+  prm.qdtype = a.qdtype;
+  prm.qrotate = a.qrotate;
+  prm.qrule = a.qrule;
   prm.H = a.H;
   prm.N = a.Nk;
   prm.Np = (int)padded_tokens(a.Nk);

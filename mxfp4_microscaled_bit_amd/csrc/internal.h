@@ -72,6 +72,13 @@ struct AttnArgs {
   float* stats_ws;   // POSTNORM, DIAG: [B, H, Np, 2] exact (m, l) of pass 1
   float* diag;       // DIAG: [B, H, N, 6]
   float gamma;       // DIAG: pre-quantization global scale of P
+  // fused Q prologue (PNQ with the UOS softmax rule only): when qx is set,
+  // qc / qs are unused and Q is rotated (qrotate) and quantized with qrule
+  // inside the forward
+  const void* qx = nullptr;
+  int qdtype = 0;
+  int64_t qsB = 0, qsH = 0, qsN = 0;
+  int qrotate = 0, qrule = 0;
 };
 
 hipError_t launch_attention(const AttnArgs& a, hipStream_t stream);

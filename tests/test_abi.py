@@ -195,3 +195,27 @@ def test_p_diagnostics_rejects_bad_arguments():
     assert dg(shape=(1, 1, 64, 32)) == 2
     assert dg(ws=None) == 7 and dg(ws_bytes=need - 1) == 7
     assert dg(out=FAKE + 4) == 4 and dg(k=FAKE + 2) == 4
+
+
+def test_forward_fused_q_rejects_bad_arguments():
+    L = mx.lib()
+
+    def fq(q=FAKE, dtype=0, shape=(1, 1, 64, 64), strides=None, k=None, v=None, causal=0, out=FAKE, stats=None):
+        k = k or _desc(0)
+        v = v or _desc(1)
+        st = None if strides is None else (ctypes.c_int64 * 3)(*strides)
+        return L.mxattn_forward_fused_q(q, dtype, mx.Shape(*shape), st, ctypes.byref(k), ctypes.byref(v), causal,
+                                        out, stats, None)
+
+    assert fq(q=None) == 1 and fq(out=None) == 1
+    assert fq(dtype=5) == 3
+    assert fq(shape=(1, 1, 64, 96)) == 2 and fq(shape=(1, 0, 64, 64)) == 2
+    assert fq(strides=(4096, 4096, 60)) == 5
+    assert fq(q=FAKE + 8) == 4 and fq(out=FAKE + 4) == 4
+    assert fq(shape=(1, 2, 64, 64)) == 6                 # heads disagree with K^
+    assert fq(shape=(1, 1, 64, 128)) == 6                # head dims disagree
+    assert fq(shape=(1, 1, 65, 64), causal=1) == 6       # causal cross-attention
+    assert fq(causal=2) == 8
+    k_ceil = mx.MXTensorDesc(FAKE, FAKE, mx.Shape(1, 1, 64, 64), 0, mx.SCALE_CEIL_Q, 1)
+    assert fq(k=k_ceil) == 8
+    assert fq(v=_desc(0)) == 6                           # V must be token blocked
