@@ -66,32 +66,43 @@ def measured_traffic(launch_bytes_algorithmic: float):
         return None
 
 
-def cpu_baseline(w, target_s: float = 12.0):
-    """The CPU oracle on a bounded sample: two heads of the workload, a number
-    of query rows each against all N keys, sized to about target_s seconds."""
+def cpu_baseline(w, target_s: float = 15.0):
+    """The CPU oracle on a bounded sample of the workload: query rows of a few
+    heads, each row against all N keys, sized to about target_s seconds (the
+    per-head quantization inside each call is part of the measured work)."""
     import numpy as np
     import oracle
     import workloads as W
 
-    heads = [(0, 0), (0, w.H // 2)]
-    sel = {t: W.generate(w, t, heads=heads)[None] for t in "qkv"}
     nth = oracle.default_threads()
+    max_heads = min(4, w.B * w.H)
+    heads = [(i // w.H, (i * max(1, w.H // max_heads)) % w.H) for i in range(max_heads)]
+    sel = {t: W.generate(w, t, heads=heads)[None] for t in "qkv"}
 
-    def run(n_rows):
+    def run(n_heads, n_rows):
         rows = np.linspace(0, w.N - 1, n_rows).astype(np.int32)
+        sub = {t: sel[t][:, :n_heads] for t in "qkv"}
         t0 = time.perf_counter()
-        oracle.attention(sel["q"], sel["k"], sel["v"], w.dtype, 1, len(heads), w.N, w.d,
+        oracle.attention(sub["q"], sub["k"], sub["v"], w.dtype, 1, n_heads, w.N, w.d,
                          causal=w.causal, kv_tile=128, rows=rows, nthreads=nth)
         return time.perf_counter() - t0
 
-    # grow the row count until one run takes about target_s (the per-head
-    # quantization inside each call is a fixed cost, so scale from the last run)
-    n_rows = 2 * nth
-    t = run(n_rows)
-    while t < target_s / 3 and n_rows < w.N:
-        n_rows = int(min(w.N, max(2 * n_rows, n_rows * target_s / max(t, 1e-3))))
-        t = run(n_rows)
-    pairs = len(heads) * n_rows * w.N  # non-causal: every row sees every key
+    # grow the sample (rows per head up to N, then heads) until one run takes
+    # a quarter of target_s; the final run scales that one to target_s, where
+    # the per-head quantization is a small part of the time
+    n_heads, n_rows = 2, 2 * nth
+    t = run(n_heads, n_rows)
+    while t < target_s / 4 and (n_rows < w.N or n_heads < max_heads):
+        if n_rows < w.N:
+            n_rows = min(w.N, 4 * n_rows)
+        else:
+            n_heads = min(max_heads, 2 * n_heads)
+        t = run(n_heads, n_rows)
+    want = n_heads * n_rows * target_s / max(t, 1e-3)  # (head, row) pairs for target_s
+    n_heads = int(min(max_heads, max(n_heads, -(-want // w.N))))
+    n_rows = int(min(w.N, max(1, want // n_heads)))
+    t = run(n_heads, n_rows)
+    pairs = n_heads * n_rows * w.N  # non-causal: every row sees every key
     flops = 4.0 * w.d * pairs
     return {
         "value": flops / t / 1e12,
@@ -99,7 +110,7 @@ def cpu_baseline(w, target_s: float = 12.0):
         "cores": nth,
         "kind": "oracle",
         "seconds": round(t, 3),
-        "sample": (f"{len(heads)} heads x {n_rows} query rows x all {w.N} keys of {w.name} "
+        "sample": (f"{n_heads} heads x {n_rows} query rows x all {w.N} keys of {w.name} "
                    f"({w.describe()}), including the oracle's own quantization of those heads; "
                    f"flops counted as 4*d per (query, key) pair"),
     }

@@ -308,6 +308,7 @@ __device__ __forceinline__ uint32_t pack_fp4x8(const float* y) {
 struct RowState {
   float m;    // running max of raw scores (or m* for POSTNORM)
   float mc;   // m * c + off
+  float mcL;  // mc + log2(7.25): the fused UOS block-scale offset
   float off;  // POSTNORM: log2 l* (P = exp(s - m*) / l*); otherwise 0
   float l;    // DIRECT / STATS: running sum of unquantized exponentials
 };
@@ -345,9 +346,8 @@ __device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, 
     // binary32 rounding moves a scale decision only within the decision
     // margin of the exp2 evaluation.  A fully masked block (-inf) takes the
     // clamp; its elements are all zero whatever the scale.
-    const float t = fmaf(bmax, F::kC, -rs.mc) - 0x1.6dd252p+1f;  // log2(7.25)
-    e = (int)__builtin_ceilf(fmaxf(t, -127.0f));
-    e = e > 127 ? 127 : e;
+    // (bmax <= m, so e <= ceil(-log2 7.25) = -2: no upper clamp)
+    e = (int)__builtin_ceilf(fmaxf(fmaf(bmax, F::kC, -rs.mcL), -127.0f));
   }
   float y[32];
   if constexpr (F::kExactArg) {
@@ -545,7 +545,11 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
 #pragma unroll
     for (int h = 0; h < NH; ++h)
       kop[t][h] = *reinterpret_cast<const uint4*>(buf + koff[h] + (D / 2) * (64 * (t >> 1) + 16 * (t & 1)));
+  // the burst of score products runs at raised wave priority, so that it
+  // reaches the matrix core ahead of the co-resident wave's vector work
   v16f s[4];
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     s[t] = v16f{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
@@ -553,6 +557,8 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
     for (int h = 0; h < NH; ++h)
       s[t] = mfma32_sel((t & 1) * NH + h, h, kop[t][h], qop[h], s[t], (t < 2) ? (int)ksw.x : (int)ksw.y, qsc);
   }
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- running max, block maxima, alpha
@@ -572,6 +578,7 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
       a = __builtin_amdgcn_exp2f((rs.m - m_new) * F::kC);  // 0 on the first visited tile
       rs.m = m_new;
       rs.mc = m_new * F::kC;
+      rs.mcL = rs.mc + 0x1.6dd252p+1f;  // log2(7.25)
     }
   }
   if constexpr (MODE == kModeStats) {
@@ -677,6 +684,7 @@ __global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Pa
   RowState rs;
   rs.m = -INFINITY;
   rs.mc = 0.0f;
+  rs.mcL = 0.0f;
   rs.off = 0.0f;
   rs.l = 0.0f;
   if constexpr (F::kFixedM) {
