@@ -12,7 +12,9 @@ Prints one JSON line.  `value` is whole-step throughput in TFLOPS, counting
 for PV).  `roofline` describes the dominant kernel (the fused forward) against
 the dense MXFP4 matrix-core peak; its duration comes from HIP events recorded
 around each forward launch on the launch stream.  `cpu_baseline` times the
-plain CPU oracle on a bounded sample of the same workload.
+plain CPU oracle on a bounded sample of the same workload.  `accuracy` gives
+the error of the output against fp32 softmax attention on the unquantized
+inputs (PyTorch on the GPU, sampled rows, outside the timed region).
 
 With --fused-q the step quantizes K and V and runs the forward entry point
 that rotates and quantizes Q in its own prologue (no Q^ buffer).
@@ -114,6 +116,39 @@ def cpu_baseline(w, target_s: float = 15.0):
                    f"({w.describe()}), including the oracle's own quantization of those heads; "
                    f"flops counted as 4*d per (query, key) pair"),
     }
+
+
+def accuracy_vs_fp32(w, dev, out, n_rows: int = 256):
+    """Error of the MXFP4 output against plain fp32 softmax attention computed
+    by PyTorch on the GPU from the same unquantized 16-bit inputs, on n_rows
+    evenly spaced query rows of two heads (outside the timed region)."""
+    import torch
+
+    B, H, N, d = w.shape
+    heads = [(0, 0), (B - 1, H // 2)]
+    rows = torch.linspace(0, N - 1, n_rows, device="cuda").round().long()
+    num = den = 0.0
+    max_abs = 0.0
+    cos = []
+    for b, h in heads:
+        q = dev["q"][b, h].index_select(0, rows).float()
+        k = dev["k"][b, h].float()
+        v = dev["v"][b, h].float()
+        s = torch.matmul(q, k.t().contiguous()) / float(d) ** 0.5
+        if w.causal:
+            keys = torch.arange(k.shape[0], device="cuda")
+            s = s.masked_fill(keys[None, :] > rows[:, None], float("-inf"))
+        ref = torch.matmul(torch.softmax(s, dim=-1), v)
+        got = out[b, h].index_select(0, rows)
+        diff = (got - ref).abs()
+        cos.append(torch.nn.functional.cosine_similarity(got, ref, dim=-1))
+        max_abs = max(max_abs, float(diff.max()))
+        num += float(diff.sum())
+        den += float(ref.abs().sum())
+    return {"reference": "fp32 softmax attention (PyTorch) on the unquantized inputs",
+            "sample": f"{n_rows} query rows x {len(heads)} heads",
+            "mean_row_cosine": round(float(torch.cat(cos).mean()), 6), "max_abs": round(max_abs, 6),
+            "mean_rel": round(num / den, 6)}
 
 
 def main():
@@ -250,6 +285,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(flops) if args.workload == 2 and not args.fused_q else None},
     }
+    result["accuracy"] = accuracy_vs_fp32(w, dev, out)
     if not args.no_cpu_baseline and Nk == N and not w.causal:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -635,7 +635,8 @@ __global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Pa
   using F = FwdConsts<D, MODE, RULE>;
   constexpr int NH = D / 64;
   constexpr int NCT = D / 32;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::STAGE];
+  constexpr int kLdsBytes = 2 * L::STAGE;  // two key/value stages
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -780,23 +781,42 @@ __global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Pa
     keep_live(done, held[0], held[1], held[2], held[3]);
     keep_live(done, one_sc);
   }
-  if (qi >= p.Nq) return;
   // O = O~ / l with a correctly rounded division (Eq. 8): with V^ constant
   // per channel, O~ = v^ l exactly, and the division returns v^ exactly
   float l;
   if constexpr (MODE == kModePnq) l = lsum;
   else if constexpr (MODE == kModeDirect) l = rs.l;
   else l = 1.0f;
-  float* orow = p.out + (bh * p.Nq + qi) * D + 4 * g;
+  // The accumulators hold, per lane, 4-float pieces of one query row; a
+  // direct store would give each 128-byte output line 32 bytes per store.
+  // Each 32-channel slice of the wave's 32 x d tile therefore goes through
+  // LDS (rows padded by 16 bytes against bank conflicts) and out as whole
+  // 128-byte row segments, eight lanes per row.
+  constexpr int RB = 32 * 4 + 16;  // staged bytes per row
+  static_assert(4 * 32 * RB <= kLdsBytes, "output staging exceeds the key/value stages");
+  uint8_t* const stg = lds + wave * 32 * RB;
+  const int srow = lane >> 3, scol = 16 * (lane & 7);
+  const int qbase = qt * kBr + 32 * wave;
+  __syncthreads();  // every wave is done with the last key/value tile
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct)
+  for (int ct = 0; ct < NCT; ++ct) {
+    const v16f& o = acc[ct];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const v16f& o = acc[ct];
-      *reinterpret_cast<float4*>(orow + 32 * ct + 8 * j) =
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(stg + r * RB + 4 * (8 * j + 4 * g)) =
           make_float4(o[4 * j] / l, o[4 * j + 1] / l, o[4 * j + 2] / l, o[4 * j + 3] / l);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int row = srow + 8 * k;
+      const float4 v = *reinterpret_cast<const float4*>(stg + row * RB + scol);
+      if (qbase + row < p.Nq)
+        *reinterpret_cast<float4*>(reinterpret_cast<uint8_t*>(p.out + (bh * p.Nq + qbase + row) * D + 32 * ct) +
+                                   scol) = v;
     }
-  if (g == 0) {
+    __syncthreads();
+  }
+  if (g == 0 && qi < p.Nq) {
     if (p.row_stats) {
       p.row_stats[(bh * p.Nq + qi) * 2 + 0] = rs.m * F::kInvSqrtD;
       p.row_stats[(bh * p.Nq + qi) * 2 + 1] = l;
