@@ -36,11 +36,14 @@ namespace {
 
 using namespace mxblock;
 
+constexpr int kHdUnitsPerThread = 1;  // row-blocks per thread of k_quantize_headdim
+
 // One lane owns one 32-channel block of one row (d/32 lanes per row, in the
 // same quad), so the first five butterfly stages stay in registers and the
 // remaining one (d=64) or two (d=128) cross lanes through DPP.  Each thread
-// handles two rows-blocks 256 lanes apart so that two 64-byte loads are in
-// flight per lane.
+// handles one row-block (64 bytes in four 16-byte loads); measured on the
+// Wan-like tensors this beats two or four blocks per thread (more
+// workgroups in flight rather than more loads per lane).
 template <int D, int DTYPE, bool ROTATE, int RULE>
 __global__ __launch_bounds__(256) void k_quantize_headdim(
     const uint16_t* __restrict__ x, int H, int N, int Np, int64_t sB, int64_t sH, int64_t sN,
@@ -48,11 +51,12 @@ __global__ __launch_bounds__(256) void k_quantize_headdim(
   constexpr int BPR = D / 32;  // blocks (lanes) per row
   static_assert(D == 64 || D == 128, "head dim");
 
-  uint4 raw[2][4];
-  int64_t unit[2];
+  constexpr int QU = kHdUnitsPerThread;
+  uint4 raw[QU][4];
+  int64_t unit[QU];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    unit[it] = (int64_t)blockIdx.x * 512 + it * 256 + threadIdx.x;
+  for (int it = 0; it < QU; ++it) {
+    unit[it] = (int64_t)blockIdx.x * 256 * QU + it * 256 + threadIdx.x;
     const int64_t row = unit[it] / BPR;
     const int blk = (int)(unit[it] % BPR);
     const int64_t bh = row / Np;
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(256) void k_quantize_headdim(
   }
 
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
+  for (int it = 0; it < QU; ++it) {
     const int blk = (int)(unit[it] % BPR);
     float v[32];
     unpack_block<DTYPE>(raw[it], v);
@@ -335,7 +339,7 @@ template <int D, int DTYPE, bool ROTATE, int RULE>
 hipError_t launch_hd(const QuantArgs& a, hipStream_t stream) {
   const int64_t Np = padded_tokens(a.N);
   const int64_t total = (int64_t)a.B * a.H * Np * (D / 32);
-  const int64_t grid = (total + 511) / 512;
+  const int64_t grid = (total + 256 * kHdUnitsPerThread - 1) / (256 * kHdUnitsPerThread);
   hipLaunchKernelGGL((k_quantize_headdim<D, DTYPE, ROTATE, RULE>), dim3((unsigned)grid), dim3(256), 0,
                      stream, static_cast<const uint16_t*>(a.x), a.H, a.N, (int)Np, a.sB, a.sH, a.sN,
                      total, a.qbits, a.codes, a.scales);
