@@ -79,7 +79,7 @@ extern "C" {
 typedef enum {
   MXATTN_OK = 0,
   MXATTN_ERR_NULL = 1,      /* a required pointer is NULL                          */
-  MXATTN_ERR_SHAPE = 2,     /* B, H or N < 1, d not 64 or 128, or sizes overflow    */
+  MXATTN_ERR_SHAPE = 2,     /* B, H or N < 1, d not 64 or 128, or B*H*Np*d > 2^36   */
   MXATTN_ERR_DTYPE = 3,     /* unknown dtype                                        */
   MXATTN_ERR_ALIGN = 4,     /* a device pointer is not 16-byte aligned              */
   MXATTN_ERR_STRIDE = 5,    /* a stride is negative or not a multiple of 8 elements */

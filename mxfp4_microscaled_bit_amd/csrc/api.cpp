@@ -16,7 +16,11 @@ static_assert(kSweepMax == MXATTN_SWEEP_MAX, "sweep capacity of the kernels and 
 
 namespace {
 
-constexpr int64_t kMaxElems = (int64_t)1 << 44;  // keeps every index and grid in range
+// At most 2^36 elements per tensor (B H Np d): every launch then stays within
+// the 32-bit work-item count of a dispatch (the forward launches B H Np / 128
+// workgroups of 256 threads, at most 2^31 work-items; the head-dim quantizer
+// one thread per 32 elements), and 64-bit indexes have ample room.
+constexpr int64_t kMaxElems = (int64_t)1 << 36;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

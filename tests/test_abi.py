@@ -39,6 +39,10 @@ def test_sizes_and_tile():
     assert mx.mx_codes_bytes(1, 1, 1, 96) == 0
     assert mx.mx_codes_bytes(1, 1, 0, 64) == 0
     assert mx.mx_codes_bytes(1, 1, 5, 64, 7) == 0
+    # at most 2^36 elements per tensor (B H Np d), so that every launch fits a dispatch
+    assert mx.mx_codes_bytes(1, 1, 2 ** 29, 128) == 2 ** 35
+    assert mx.mx_codes_bytes(1, 2, 2 ** 29, 128) == 0
+    assert mx.mx_codes_bytes(2 ** 20, 1, 2 ** 9, 128) == 2 ** 35 and mx.mx_codes_bytes(2 ** 20, 1, 2 ** 9 + 1, 128) == 0
     assert mx.forward_kv_tile(128) == 128 and mx.forward_kv_tile(64, True) == 128
     assert mx.forward_kv_tile(80) == 0
     ws = mx.reference_modes_workspace_bytes(1, 2, 256, 128, mx.P_POSTNORM)
