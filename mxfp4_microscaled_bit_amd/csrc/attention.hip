@@ -626,31 +626,20 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   }
 }
 
-// Two workgroups (two waves per SIMD) per CU; the diagnostics pass keeps
-// more per-element state and runs with one, which gives it the accumulation
-// registers instead of scratch spills.
+template <int D>
+constexpr int kLdsBytes = 2 * Lds<D>::STAGE;  // two key/value stages
+
+// One query tile (128 queries of head bh): the whole online-softmax pass over
+// its key tiles and the epilogue.
 template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ>
-__global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Params p) {
+__device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, int64_t bh, int qt, int tid) {
   using L = Lds<D>;
   using F = FwdConsts<D, MODE, RULE>;
   constexpr int NH = D / 64;
   constexpr int NCT = D / 32;
-  constexpr int kLdsBytes = 2 * L::STAGE;  // two key/value stages
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-
-  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, g = lane >> 5;
 
-  // workgroup -> (head, query tile); consecutive logical tiles land on the
-  // same XCD (the hardware deals workgroups round-robin over 8 XCDs) so the
-  // query tiles of one head share that XCD's L2 copy of its K^ and V^
-  const int G = gridDim.x, bid = blockIdx.x;
-  const int xcd = bid & 7, idx = bid >> 3, qx = G >> 3, rx = G & 7;
-  const int logical = (xcd < rx) ? xcd * (qx + 1) + idx : rx * (qx + 1) + (xcd - rx) * qx + idx;
-  const int64_t bh = logical / p.nqt;
-  int qt = logical % p.nqt;
-  if (CAUSAL) qt = p.nqt - 1 - qt;  // longest causal rows first
   const int nkt_all = (p.N + kBc - 1) / kBc;
   const int nkt = CAUSAL ? min(qt + 1, nkt_all) : nkt_all;
   // leading tiles in which every key is visible to every query of the tile
@@ -793,7 +782,7 @@ __global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Pa
   // LDS (rows padded by 16 bytes against bank conflicts) and out as whole
   // 128-byte row segments, eight lanes per row.
   constexpr int RB = 32 * 4 + 16;  // staged bytes per row
-  static_assert(4 * 32 * RB <= kLdsBytes, "output staging exceeds the key/value stages");
+  static_assert(4 * 32 * RB <= kLdsBytes<D>, "output staging exceeds the key/value stages");
   uint8_t* const stg = lds + wave * 32 * RB;
   const int srow = lane >> 3, scol = 16 * (lane & 7);
   const int qbase = qt * kBr + 32 * wave;
@@ -825,9 +814,39 @@ __global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Pa
   }
 }
 
+// Workgroup -> (head, query tiles).  Consecutive logical indexes land on the
+// same XCD (the hardware deals workgroups round-robin over the 8 XCDs), so
+// the query tiles of one head share that XCD's L2 copy of its K^ and V^.
+// Under the causal mask query tile t visits t + 1 key tiles; a workgroup
+// takes the pair (nqt - 1 - i, i), nqt + 1 key tiles in all, so every
+// workgroup has the same work (the middle tile of an odd count runs alone).
+// Two workgroups (two waves per SIMD) per CU; the diagnostics pass keeps more
+// per-element state and runs with one, which gives it the accumulation
+// registers instead of scratch spills.
+template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ>
+__global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Params p) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes<D>];
+  const int tid = threadIdx.x;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3, qx = G >> 3, rx = G & 7;
+  const int logical = (xcd < rx) ? xcd * (qx + 1) + idx : rx * (qx + 1) + (xcd - rx) * qx + idx;
+  if constexpr (CAUSAL) {
+    const int npair = (p.nqt + 1) / 2;
+    const int64_t bh = logical / npair;
+    const int i = logical % npair;
+    attention_qtile<D, CAUSAL, MODE, RULE, FUSEDQ>(p, lds, bh, p.nqt - 1 - i, tid);
+    if (i != p.nqt - 1 - i) {
+      __syncthreads();  // every wave is done with the LDS stages
+      attention_qtile<D, CAUSAL, MODE, RULE, FUSEDQ>(p, lds, bh, i, tid);
+    }
+  } else {
+    attention_qtile<D, CAUSAL, MODE, RULE, FUSEDQ>(p, lds, logical / p.nqt, logical % p.nqt, tid);
+  }
+}
+
 template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ = false>
 hipError_t launch_one(const Params& prm, int BH, hipStream_t stream) {
-  const int64_t groups = (int64_t)BH * prm.nqt;
+  const int64_t groups = (int64_t)BH * (CAUSAL ? (prm.nqt + 1) / 2 : prm.nqt);
   hipLaunchKernelGGL((k_attention<D, CAUSAL, MODE, RULE, FUSEDQ>), dim3((unsigned)groups), dim3(256), 0, stream,
                      prm);
   return hipGetLastError();
