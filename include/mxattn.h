@@ -4,12 +4,12 @@
  *
  * The method (MXAttention, "Data-Free Optimal Scaling and Pre-Normalization
  * Quantization for MXFP4 Attention"):
- *   1. a fixed Hadamard rotation of Q and K (Sec. 4.3, Alg. 2 steps 3-4);
+ *   1. a fixed Hadamard rotation of Q and K (Sec. 4.3, Alg. 2);
  *   2. MXFP4 quantization of Q, K and V -- 32-element blocks of E2M1 values
  *      sharing one E8M0 scale chosen by Universal Optimal Scaling,
- *      e = ceil(log2(M / 7.25)) (Sec. 4.1, Alg. 1; Alg. 2 steps 5-7);
+ *      e = ceil(log2(M / 7.25)) (Sec. 4.1, Alg. 1; Alg. 2);
  *   3. block-scaled FP4 matrix products QK^T and PV inside a tiled online
- *      softmax (Sec. 2, Eqs. 2-8; Alg. 2 steps 8-21);
+ *      softmax (Sec. 2, Eqs. 2-8; Alg. 2);
  *   4. Pre-Normalization Quantization: the unnormalized exponential tile
  *      exp(S - m) is quantized once, and that same quantized tile updates both
  *      the row sum l and the output accumulator (Sec. 4.2, Eqs. 44-48).
@@ -129,7 +129,7 @@ size_t mxattn_mx_codes_bytes(mxattn_shape shape, int32_t axis);
 size_t mxattn_mx_scales_bytes(mxattn_shape shape, int32_t axis);
 
 /* Width B_c of the key/value tiles of the online-softmax loop of
- * mxattn_forward (Alg. 2 step 10).  PNQ quantizes each exponential tile
+ * mxattn_forward (Alg. 2).  PNQ quantizes each exponential tile
  * against the running maximum reached after that tile, so the result depends
  * on B_c: it is part of the definition of the output.  Tiles are visited in
  * ascending key order; the exponentials are quantized in 32-key blocks
@@ -140,11 +140,11 @@ int32_t mxattn_forward_kv_tile(int32_t d, int32_t causal);
  *   x        device pointer to the [B, H, N, d] 16-bit input
  *   dtype    mxattn_dtype
  *   strides  host array of 3 element strides (B, H, N) or NULL (contiguous)
- *   axis     MXATTN_AXIS_HEAD_DIM (Q, K; Alg. 2 steps 5-6, blocks along d)
- *            or MXATTN_AXIS_TOKEN (V; Alg. 2 step 7, blocks along tokens --
+ *   axis     MXATTN_AXIS_HEAD_DIM (Q, K; Alg. 2, blocks along d)
+ *            or MXATTN_AXIS_TOKEN (V; Alg. 2, blocks along tokens --
  *            the block axis of the PV product's contraction, as the MatX
  *            "leaky quantization" page describes)
- *   rotate   1: apply the Hadamard rotation first (Alg. 2 steps 3-4); only
+ *   rotate   1: apply the Hadamard rotation first (Alg. 2); only
  *            allowed with MXATTN_AXIS_HEAD_DIM
  *   rule     mxattn_scale_rule
  *   out      host descriptor: the caller sets out->codes and out->scales to
@@ -191,7 +191,7 @@ mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shap
                                  const double* q_values, int32_t n_q, double* sse,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Fused MXFP4 attention forward with PNQ (Alg. 2 steps 8-22).
+/* Fused MXFP4 attention forward with PNQ (Alg. 2).
  *   q        head-dimension MXFP4 tensor, shape [B, H, Nq, d]
  *   k        head-dimension MXFP4 tensor, shape [B, H, Nk, d]; both q and k
  *            rotated or both not (Q K^T is unchanged by the rotation only if
@@ -215,7 +215,7 @@ mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* 
 
 /* mxattn_forward with the Q preprocessing fused into its prologue: the
  * paper puts the Hadamard rotation inside the Q/K preprocessing stage at
- * negligible cost (Sec. 4.3; Alg. 2 steps 3-6).  Each workgroup rotates (if
+ * negligible cost (Sec. 4.3; Alg. 2).  Each workgroup rotates (if
  * k->rotated) and quantizes its own query rows with k's rule, exactly as
  * mxattn_rotate_quantize would (bit for bit), and keeps Q^ on chip: no Q^
  * buffer, no separate launch.  The output equals that of

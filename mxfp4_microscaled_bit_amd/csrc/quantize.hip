@@ -1,11 +1,11 @@
 // MXFP4 quantizers of MXAttention for gfx950 (MI355X).
 //
 //   k_quantize_headdim: Q and K.  Optional Hadamard rotation along the head
-//     dimension (MXAttention paper, Sec. 4.3, Alg. 2 steps 3-4), then UOS or
-//     OCP block quantization of every 32 consecutive channels (Alg. 1; Alg. 2
-//     steps 5-6).
+//     dimension (MXAttention paper, Sec. 4.3, Alg. 2), then UOS or
+//     OCP block quantization of every 32 consecutive channels (Alg. 1;
+//     Alg. 2).
 //   k_quantize_tokens: V.  Block quantization along tokens, 32 consecutive
-//     tokens of one channel per block (Alg. 2 step 7, with the block axis that
+//     tokens of one channel per block (Alg. 2, with the block axis that
 //     the PV product contracts over, as the MatX leaky-quantization page
 //     explains).
 //   k_sweep_headdim / k_sweep_tokens + k_sweep_reduce: the per-head squared

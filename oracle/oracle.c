@@ -225,7 +225,7 @@ static void strides_or_contig(const int64_t* strides, int H, int N, int d, int64
 }
 
 /* One Q/K row: decode, optionally rotate (binary32), then quantize each
- * 32-channel block along the head dimension [P1 Alg. 2 steps 3-6]. */
+ * 32-channel block along the head dimension [P1 Alg. 2]. */
 static void quantize_row(const qrows_ctx* c, int64_t g, uint8_t* codes, uint8_t* scales, float* buf) {
   int64_t bh = g / c->N, n = g % c->N;
   int64_t b = bh / c->H, h = bh % c->H;
@@ -547,7 +547,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
     const int i = c->rows ? c->rows[r] : r;
     load_query(c, b, h, i, qv, buf, codes, blk);
     const int jvis = g->causal ? (i + 1 < N ? i + 1 : N) : N; /* keys [0, jvis) visible */
-    /* S_ij = q^ . k^_j / sqrt(d) [P1 Eq. 2, Alg. 2 step 11] */
+    /* S_ij = q^ . k^_j / sqrt(d) [P1 Eq. 2, Alg. 2] */
     for (int j = 0; j < jvis; ++j) {
       double acc = 0.0;
       for (int t = 0; t < d; ++t) acc += qv[t] * K[(int64_t)j * d + t];
@@ -588,7 +588,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
       continue;
     }
 
-    /* Online softmax over key tiles in ascending order [P1 Alg. 2 steps 9-19;
+    /* Online softmax over key tiles in ascending order [P1 Alg. 2;
      * Eqs. 3-7 with Eqs. 44-48 (PNQ) or Eq. 42 (direct)]. */
     double m = -INFINITY, l = 0.0, al = 0.0;
     int ntiles_seen = 0;
@@ -637,10 +637,10 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
         al = alpha * al + dl;
       }
       tm[tile] = m_new; th[tile] = sum_hat; tt[tile] = sum_til;
-      m = m_new;                                                /* step 18 */
+      m = m_new;                                     /* the running maximum moves on */
     }
     (void)ntiles_seen;
-    /* O_i = o / l  [Eq. 8; Alg. 2 step 20]; POSTNORM without quantization
+    /* O_i = o / l  [Eq. 8; Alg. 2]; POSTNORM without quantization
      * reduces to the same exact softmax attention. */
     for (int ch = 0; ch < d; ++ch) orow[ch] = o[ch] / l;
     if (mrow) for (int ch = 0; ch < d; ++ch) mrow[ch] = am[ch] / l;

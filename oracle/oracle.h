@@ -81,7 +81,7 @@ float oracle_decode_half(uint16_t bits, int dtype);
 
 /* x <- x * H_d / sqrt(d) for one row of length d (a power of two), where H_d
  * is the Sylvester Hadamard matrix, H[i][j] = (-1)^popcount(i & j)
- * [P1 Sec. 4.3, Alg. 2 steps 3-4; P2 "Rotate Q and K"].  Evaluated in
+ * [P1 Sec. 4.3, Alg. 2; P2 "Rotate Q and K"].  Evaluated in
  * binary32: butterflies with strides 1, 2, 4, ..., d/2, each output one
  * correctly rounded add or subtract, then one multiply by fl32(1/sqrt(d)). */
 void oracle_hadamard_rotate_f32(float* x, int d);

@@ -74,7 +74,7 @@ def test_decision_boundaries_and_ties_match_page():
 
 
 def test_sign_and_zero_blocks():
-    # all-zero block: sigma = 1 and every element 0 [P1 Sec. 2 end; Alg. 1 steps 4-7]
+    # all-zero block: sigma = 1 and every element 0 [P1 Sec. 2 end; Alg. 1]
     sb, codes, e = oracle.quantize_block(np.zeros(32))
     assert sb == 127 and e == 0 and not codes.any()
     # negative zero keeps its sign bit (reading of the pages' silence on signed zero)
@@ -317,7 +317,7 @@ def test_ocp_overflow_region_probability():
 
 
 # --------------------------------------------------------------------------
-# element decode and Hadamard rotation  [P1 Sec. 4.3, Alg. 2 steps 3-4; P2]
+# element decode and Hadamard rotation  [P1 Sec. 4.3, Alg. 2; P2]
 
 
 def test_decode_half_exhaustive():
