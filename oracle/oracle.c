@@ -39,7 +39,7 @@ double oracle_e2m1_value(int code) {
   return (code & 8) ? -v : v;
 }
 
-/* Round-to-nearest projection onto the finite grid [P1 Eq. 10].  The nearest
+/* Nearest E2M1 grid point of y >= 0 [P1 Eq. 10].  The nearest
  * neighbour is decided by comparing with the midpoint of two adjacent grid
  * points (the decision boundaries of Eq. 68), which is exact in binary64.
  * Above the last midpoint every value maps to the largest element, 6: this is

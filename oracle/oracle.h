@@ -57,9 +57,9 @@ double oracle_e2m1_magnitude(int code);
 /* Signed value of a 4-bit code: bit 3 is the sign, bits 0..2 the magnitude. */
 double oracle_e2m1_value(int code);
 
-/* Round-to-nearest projection of y >= 0 onto the finite E2M1 grid, values
- * beyond the grid saturating at 6 [P1 Eq. 10]; an exact tie goes to the even
- * code.  Returns the magnitude code 0..7. */
+/* The E2M1 grid point nearest to y >= 0, with every y above the largest
+ * grid value mapped to 6 [P1 Eq. 10]; an exact tie goes to the even code.
+ * Returns the magnitude code 0..7. */
 int oracle_e2m1_project(double y);
 
 /* Shared-scale exponent for block maximum M > 0 under `rule` (q is read by

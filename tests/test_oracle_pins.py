@@ -140,7 +140,8 @@ def test_normalized_max_ranges_exhaustive_bf16_and_random_fp32():
 
 
 def test_oas_equivalent_rule_relation():
-    """App. G, Eq. 96: e_7 = e_6 - 1 when x_6 in (3, 3.5], else e_6."""
+    """App. G, Eq. 96: the q = 7 exponent is one below the q = 6 (TFS)
+    exponent exactly for blocks whose TFS-normalized max lies in (3, 3.5]."""
     M = _positive_bf16()
     e6 = oracle.scale_exponents(M, oracle.RULE_CEIL_Q, 6.0)
     e7 = oracle.scale_exponents(M, oracle.RULE_CEIL_Q, 7.0)
