@@ -219,22 +219,29 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    # events (on the launch stream) around the step's parts: e[0] start,
+    # e[1] after Q's quantizer, e[2] after K's, e[3] after V's, e[4] after the
+    # forward
     def step(record=None):
-        e = [ev() for _ in range(3)] if record is not None else None
+        e = [ev() for _ in range(5)] if record is not None else None
         if e:
             e[0].record(stream)
         if not args.fused_q:
             mx.rotate_quantize(dev["q"], mx.AXIS_HEAD_DIM, rotate=True, out=qm)
-        mx.rotate_quantize(dev["k"], mx.AXIS_HEAD_DIM, rotate=True, out=km)
-        mx.rotate_quantize(dev["v"], mx.AXIS_TOKEN, rotate=False, out=vm)
         if e:
             e[1].record(stream)
+        mx.rotate_quantize(dev["k"], mx.AXIS_HEAD_DIM, rotate=True, out=km)
+        if e:
+            e[2].record(stream)
+        mx.rotate_quantize(dev["v"], mx.AXIS_TOKEN, rotate=False, out=vm)
+        if e:
+            e[3].record(stream)
         if args.fused_q:
             mx.forward_fused_q(dev["q"], km, vm, causal=w.causal, out=out)
         else:
             mx.forward(qm, km, vm, causal=w.causal, out=out)
         if e:
-            e[2].record(stream)
+            e[4].record(stream)
             record.append(e)
 
     for _ in range(args.warmup):
@@ -247,14 +254,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    quant_ms = sum(e[0].elapsed_time(e[1]) for e in events) / len(events)
-    fwd_ms = sum(e[1].elapsed_time(e[2]) for e in events) / len(events)
+    quant_ms = sum(e[0].elapsed_time(e[3]) for e in events) / len(events)
+    k_ms = sum(e[1].elapsed_time(e[2]) for e in events) / len(events)  # K's rotate + quantize
+    v_ms = sum(e[2].elapsed_time(e[3]) for e in events) / len(events)  # V's quantize
+    fwd_ms = sum(e[3].elapsed_time(e[4]) for e in events) / len(events)
     ms_per_step = wall * 1000.0 / args.steps
     flops = w.flops()
     value = flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
     quant_bytes = B * H * ((0 if args.fused_q else N) + 2 * Nk) * d * QUANT_BYTES_PER_ELEMENT
     quant_gbs = quant_bytes / (quant_ms * 1e-3) / 1e9
+
+    def per_launch(ms, elements):
+        gbs = elements * QUANT_BYTES_PER_ELEMENT / (ms * 1e-3) / 1e9
+        return {"us": round(ms * 1e3, 2), "gb_per_s": round(gbs, 1), "frac_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
     result = {
         "metric": "fused MXFP4 attention fwd TFLOPS (1 GPU) + % of MXFP4 MFMA peak; quantizer GB/s",
@@ -280,7 +293,11 @@ def main():
                     "frac_mfma_peak": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4)},
         "quantizer": {"ms": round(quant_ms, 4), "gb_per_s": round(quant_gbs, 1),
                       "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
-                      "bytes": quant_bytes},
+                      "bytes": quant_bytes,
+                      # one launch each: K's rotate+quantize (head-dim blocks) and
+                      # V's quantize (token blocks), event-timed on the stream
+                      "rotate_quantize_k": per_launch(k_ms, B * H * Nk * d),
+                      "quantize_v": per_launch(v_ms, B * H * Nk * d)},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(flops) if args.workload == 2 and not args.fused_q else None},
