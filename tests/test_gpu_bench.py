@@ -1,0 +1,48 @@
+"""The benchmark's output contract on the GPU: one JSON line with the agreed
+fields, consistent units and a roofline entry, from a short run of the
+small workload (the full Wan-like run is the benchmark itself)."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(*args):
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True, text=True,
+                       timeout=240)
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+    assert len(lines) == 1, r.stdout
+    return json.loads(lines[0])
+
+
+@pytest.mark.gpu
+def test_bench_json_line():
+    d = _run("--workload", "1", "--steps", "2", "--warmup", "1", "--no-cpu-baseline")
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step", "higher_is_better",
+                "scaling", "vs_baseline", "dtype", "data", "config", "roofline", "forward", "quantizer", "accuracy"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 2 and d["warmup"] == 1
+    assert d["unit"] == "TFLOPS" and d["higher_is_better"] is True and d["data"] == "synthetic"
+    assert d["value"] > 0 and d["ms_per_step"] > 0
+    assert d["config"]["workload"].startswith("tiny_outliers")
+    rf = d["roofline"]
+    assert rf["bound"] == "mfma" and rf["unit"] == "TFLOP/s" and rf["peak"] == 10100.0
+    assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
+    assert rf["achieved"] == d["forward"]["tflops"]
+    q = d["quantizer"]
+    assert q["gb_per_s"] > 0 and 0 < q["frac_hbm_peak"] < 1
+    assert q["rotate_quantize_k"]["us"] > 0 and q["quantize_v"]["us"] > 0
+    a = d["accuracy"]
+    assert -1.0 <= a["mean_row_cosine"] <= 1.0 and a["max_abs"] >= 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """(CPU) the one-GPU scope is enforced before any GPU work."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
