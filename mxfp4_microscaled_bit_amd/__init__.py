@@ -137,10 +137,39 @@ def reference_modes_workspace_bytes(B, H, N, d, p_mode) -> int:
     return lib().mxattn_reference_modes_workspace_bytes(_shape(B, H, N, d), p_mode)
 
 
-def _stream(stream):
+def _device(*tensors) -> torch.device:
+    """The one device every given tensor lives on.  The library receives raw
+    device addresses and launches on the current device, so host tensors and
+    tensors of different devices are refused here."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"libmxattn takes device tensors; got one on {t.device}")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"tensors on {dev} and on {t.device}: all must be on one device")
+    return dev
+
+
+def _stream(stream, dev: torch.device):
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif stream.device != dev:
+        raise ValueError(f"stream on {stream.device}, tensors on {dev}")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _buffer(t: torch.Tensor, nbytes: int, what: str):
+    """An output or workspace tensor the library writes: contiguous and at
+    least nbytes long (the C ABI cannot see buffer lengths)."""
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise ValueError(f"{what} holds {have} bytes; {nbytes} are needed")
 
 
 def _dtype_enum(t: torch.Tensor) -> int:
@@ -179,6 +208,11 @@ class MXTensor:
                    torch.empty(sb, dtype=torch.uint8, device=device), (B, H, N, d), axis)
 
     def desc(self) -> MXTensorDesc:
+        """The C descriptor, after checking that codes and scales are
+        contiguous device buffers long enough for the shape."""
+        _device(self.codes, self.scales)
+        _buffer(self.codes, mx_codes_bytes(*self.shape, self.axis), "MXFP4 codes")
+        _buffer(self.scales, mx_scales_bytes(*self.shape, self.axis), "MXFP4 scales")
         return MXTensorDesc(self.codes.data_ptr(), self.scales.data_ptr(), _shape(*self.shape),
                             self.axis, self.rule, self.rotated)
 
@@ -187,12 +221,16 @@ def rotate_quantize(x: torch.Tensor, axis: int = AXIS_HEAD_DIM, rotate: bool = T
                     rule: int = SCALE_UOS, out: MXTensor | None = None, stream=None) -> MXTensor:
     """mxattn_rotate_quantize on a [B, H, N, d] bf16/fp16 device tensor."""
     B, H, N, d = x.shape
+    dev = _device(x)
     if out is None:
-        out = MXTensor.empty(B, H, N, d, axis, device=x.device)
+        out = MXTensor.empty(B, H, N, d, axis, device=dev)
+    out.shape, out.axis = (B, H, N, d), axis
+    _device(x, out.codes, out.scales)
     desc = out.desc()
-    _check(lib().mxattn_rotate_quantize(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d),
-                                        _strides(x), axis, int(bool(rotate)), rule, ctypes.byref(desc),
-                                        _stream(stream)), "mxattn_rotate_quantize")
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_rotate_quantize(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d),
+                                            _strides(x), axis, int(bool(rotate)), rule, ctypes.byref(desc),
+                                            _stream(stream, dev)), "mxattn_rotate_quantize")
     out.shape, out.axis, out.rule, out.rotated = (B, H, N, d), axis, rule, int(bool(rotate))
     return out
 
@@ -201,12 +239,16 @@ def rotate_quantize_q(x: torch.Tensor, q_max: float, axis: int = AXIS_HEAD_DIM, 
                       out: MXTensor | None = None, stream=None) -> MXTensor:
     """mxattn_rotate_quantize_q: the ceiling rule e = ceil(log2(M / q_max))."""
     B, H, N, d = x.shape
+    dev = _device(x)
     if out is None:
-        out = MXTensor.empty(B, H, N, d, axis, device=x.device)
+        out = MXTensor.empty(B, H, N, d, axis, device=dev)
+    out.shape, out.axis = (B, H, N, d), axis
+    _device(x, out.codes, out.scales)
     desc = out.desc()
-    _check(lib().mxattn_rotate_quantize_q(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d),
-                                          _strides(x), axis, int(bool(rotate)), float(q_max), ctypes.byref(desc),
-                                          _stream(stream)), "mxattn_rotate_quantize_q")
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_rotate_quantize_q(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d),
+                                              _strides(x), axis, int(bool(rotate)), float(q_max),
+                                              ctypes.byref(desc), _stream(stream, dev)), "mxattn_rotate_quantize_q")
     out.shape, out.axis, out.rule, out.rotated = (B, H, N, d), axis, SCALE_CEIL_Q, int(bool(rotate))
     return out
 
@@ -221,16 +263,22 @@ def scale_sweep(x: torch.Tensor, q_values, axis: int = AXIS_HEAD_DIM, rotate: bo
     """mxattn_scale_sweep: per-head sum of squared quantization errors for each
     boundary; returns float64 [B*H, len(q_values)] on the device."""
     B, H, N, d = x.shape
+    dev = _device(x)
     qs = (ctypes.c_double * len(q_values))(*[float(q) for q in q_values])
     if out is None:
-        out = torch.empty((B * H, len(q_values)), dtype=torch.float64, device=x.device)
+        out = torch.empty((B * H, len(q_values)), dtype=torch.float64, device=dev)
     need = scale_sweep_workspace_bytes(B, H, N, d, axis, len(q_values))
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
-    _check(lib().mxattn_scale_sweep(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d), _strides(x),
-                                    axis, int(bool(rotate)), qs, len(q_values), ctypes.c_void_p(out.data_ptr()),
-                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)),
-           "mxattn_scale_sweep")
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _device(x, out, workspace)
+    _buffer(out, B * H * len(q_values) * 8, "out")
+    _buffer(workspace, 0, "workspace")
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_scale_sweep(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d),
+                                        _strides(x), axis, int(bool(rotate)), qs, len(q_values),
+                                        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+                                        workspace.numel() * workspace.element_size(), _stream(stream, dev)),
+               "mxattn_scale_sweep")
     return out
 
 
@@ -246,11 +294,13 @@ def forward(q: MXTensor, k: MXTensor, v: MXTensor, causal: bool = False, out: to
     if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
                                   or row_stats.numel() != B * H * N * 2):
         raise ValueError("row_stats must be a contiguous float32 [B, H, N, 2] tensor")
+    dev = _device(q.codes, q.scales, k.codes, k.scales, v.codes, v.scales, out, row_stats)
     dq, dk, dv = q.desc(), k.desc(), v.desc()
-    _check(lib().mxattn_forward(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(causal)),
-                                ctypes.c_void_p(out.data_ptr()),
-                                None if row_stats is None else ctypes.c_void_p(row_stats.data_ptr()),
-                                _stream(stream)), "mxattn_forward")
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_forward(ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), int(bool(causal)),
+                                    ctypes.c_void_p(out.data_ptr()),
+                                    None if row_stats is None else ctypes.c_void_p(row_stats.data_ptr()),
+                                    _stream(stream, dev)), "mxattn_forward")
     return out
 
 
@@ -268,12 +318,14 @@ def forward_fused_q(q: torch.Tensor, k: MXTensor, v: MXTensor, causal: bool = Fa
     if row_stats is not None and (row_stats.dtype != torch.float32 or not row_stats.is_contiguous()
                                   or row_stats.numel() != B * H * N * 2):
         raise ValueError("row_stats must be a contiguous float32 [B, H, N, 2] tensor")
+    dev = _device(q, k.codes, k.scales, v.codes, v.scales, out, row_stats)
     dk, dv = k.desc(), v.desc()
-    _check(lib().mxattn_forward_fused_q(
-        ctypes.c_void_p(q.data_ptr()), _dtype_enum(q), _shape(B, H, N, d), _strides(q), ctypes.byref(dk),
-        ctypes.byref(dv), int(bool(causal)), ctypes.c_void_p(out.data_ptr()),
-        None if row_stats is None else ctypes.c_void_p(row_stats.data_ptr()), _stream(stream)),
-        "mxattn_forward_fused_q")
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_forward_fused_q(
+            ctypes.c_void_p(q.data_ptr()), _dtype_enum(q), _shape(B, H, N, d), _strides(q), ctypes.byref(dk),
+            ctypes.byref(dv), int(bool(causal)), ctypes.c_void_p(out.data_ptr()),
+            None if row_stats is None else ctypes.c_void_p(row_stats.data_ptr()), _stream(stream, dev)),
+            "mxattn_forward_fused_q")
     return out
 
 
@@ -287,17 +339,24 @@ def quantize_reference_modes(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, 
     if q.stride() != k.stride() or q.stride() != v.stride():
         raise ValueError("q, k, v must share strides")
     B, H, N, d = q.shape
+    dev = _device(q, k, v)
     if out is None:
-        out = torch.empty((B, H, N, d), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, H, N, d), dtype=torch.float32, device=dev)
     need = reference_modes_workspace_bytes(B, H, N, d, p_mode)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check(lib().mxattn_quantize_reference_modes(
-        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
-        _dtype_enum(q), _shape(B, H, N, d), _strides(q), rule, p_mode, int(bool(rotate)), int(bool(causal)),
-        ctypes.c_void_p(out.data_ptr()), None if row_sums is None else ctypes.c_void_p(row_sums.data_ptr()),
-        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)),
-        "mxattn_quantize_reference_modes")
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _device(q, k, v, out, row_sums, workspace)
+    _buffer(out, B * H * N * d * 4, "out")
+    if row_sums is not None:
+        _buffer(row_sums, B * H * N * 4, "row_sums")
+    _buffer(workspace, 0, "workspace")
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_quantize_reference_modes(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            _dtype_enum(q), _shape(B, H, N, d), _strides(q), rule, p_mode, int(bool(rotate)), int(bool(causal)),
+            ctypes.c_void_p(out.data_ptr()), None if row_sums is None else ctypes.c_void_p(row_sums.data_ptr()),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+            _stream(stream, dev)), "mxattn_quantize_reference_modes")
     return out
 
 
@@ -313,15 +372,21 @@ def p_diagnostics(q: torch.Tensor, k: torch.Tensor, rule: int = SCALE_UOS, rotat
     if q.shape != k.shape or q.dtype != k.dtype or q.stride() != k.stride():
         raise ValueError("q and k must share shape, dtype and strides")
     B, H, N, d = q.shape
+    dev = _device(q, k)
     if out is None:
-        out = torch.empty((B, H, N, 6), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, H, N, 6), dtype=torch.float32, device=dev)
     need = p_diagnostics_workspace_bytes(B, H, N, d)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _check(lib().mxattn_p_diagnostics(
-        ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), _dtype_enum(q), _shape(B, H, N, d), _strides(q),
-        rule, int(bool(rotate)), int(bool(causal)), float(gamma), ctypes.c_void_p(out.data_ptr()),
-        ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), _stream(stream)), "mxattn_p_diagnostics")
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _device(q, k, out, workspace)
+    _buffer(out, B * H * N * 6 * 4, "out")
+    _buffer(workspace, 0, "workspace")
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_p_diagnostics(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), _dtype_enum(q), _shape(B, H, N, d),
+            _strides(q), rule, int(bool(rotate)), int(bool(causal)), float(gamma), ctypes.c_void_p(out.data_ptr()),
+            ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size(),
+            _stream(stream, dev)), "mxattn_p_diagnostics")
     return out
 
 

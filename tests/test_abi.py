@@ -223,3 +223,38 @@ def test_forward_fused_q_rejects_bad_arguments():
     k_ceil = mx.MXTensorDesc(FAKE, FAKE, mx.Shape(1, 1, 64, 64), 0, mx.SCALE_CEIL_Q, 1)
     assert fq(k=k_ceil) == 8
     assert fq(v=_desc(0)) == 6                           # V must be token blocked
+
+
+def test_binding_refuses_host_tensors_before_any_call():
+    """The library receives raw addresses and launches on the current device:
+    the binding refuses host tensors (whose addresses a kernel cannot read)
+    before anything reaches the library."""
+    import torch
+    x = torch.zeros(1, 1, 128, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device tensors"):
+        mx.rotate_quantize(x)
+    with pytest.raises(ValueError, match="device tensors"):
+        mx.scale_sweep(x, [7.25])
+    with pytest.raises(ValueError, match="device tensors"):
+        mx.quantize_reference_modes(x, x, x)
+    with pytest.raises(ValueError, match="device tensors"):
+        mx.p_diagnostics(x, x)
+    with pytest.raises(ValueError, match="device tensors"):
+        mx._device(torch.zeros(1, device="meta"))
+    host = mx.MXTensor(torch.zeros(4096, dtype=torch.uint8), torch.zeros(256, dtype=torch.uint8), (1, 1, 128, 64),
+                       mx.AXIS_HEAD_DIM)
+    with pytest.raises(ValueError, match="device tensors"):
+        host.desc()
+    with pytest.raises(ValueError, match="device tensors"):
+        mx.forward(host, host, host, out=torch.zeros(1, 1, 128, 64))
+
+
+def test_binding_buffer_lengths():
+    """Outputs and workspaces must be contiguous and long enough: the C ABI
+    cannot see their lengths."""
+    import torch
+    mx._buffer(torch.zeros(16, dtype=torch.float32), 64, "out")
+    with pytest.raises(ValueError, match="holds 60 bytes; 64 are needed"):
+        mx._buffer(torch.zeros(15, dtype=torch.float32), 64, "out")
+    with pytest.raises(ValueError, match="contiguous"):
+        mx._buffer(torch.zeros(8, 8)[:, ::2], 16, "out")

@@ -167,3 +167,23 @@ def test_quantizer_is_deterministic():
     b = mx.rotate_quantize(dev, mx.AXIS_HEAD_DIM)
     torch.cuda.synchronize()
     assert torch.equal(a.codes, b.codes) and torch.equal(a.scales, b.scales)
+
+
+def test_binding_rejects_short_buffers_before_launch():
+    """A caller-provided MXFP4 tensor or output too short for the call is
+    refused before any kernel runs."""
+    say("binding: short buffers are refused")
+    x = torch.zeros(1, 1, 256, 128, dtype=torch.bfloat16, device="cuda")
+    short = mx.MXTensor(torch.empty(100, dtype=torch.uint8, device="cuda"),
+                        torch.empty(100, dtype=torch.uint8, device="cuda"), (1, 1, 256, 128), mx.AXIS_HEAD_DIM)
+    with pytest.raises(ValueError, match="bytes"):
+        mx.rotate_quantize(x, out=short)
+    good = mx.rotate_quantize(x)
+    v = mx.rotate_quantize(x, mx.AXIS_TOKEN, rotate=False)
+    with pytest.raises(ValueError, match="bytes"):
+        mx.forward(short, good, v)
+    with pytest.raises(ValueError, match="bytes"):
+        mx.scale_sweep(x, [6.0, 7.25], out=torch.empty(1, dtype=torch.float64, device="cuda"))
+    with pytest.raises(ValueError, match="bytes"):
+        mx.p_diagnostics(x, x, out=torch.empty(10, dtype=torch.float32, device="cuda"))
+    torch.cuda.synchronize()
