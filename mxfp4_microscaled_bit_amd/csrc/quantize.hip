@@ -36,6 +36,17 @@ namespace {
 
 using namespace mxblock;
 
+// 16-byte store with the non-temporal hint.  The head-dim quantizer writes its
+// code bytes this way (nothing in the kernel reads them back).  Measured on
+// the MI355X: that launch alone runs about 4 % faster, and the Q, K, V
+// quantizer launches of one step about 1.5 % faster in total.  The token-axis
+// quantizer measured slightly slower with the hint and keeps plain stores.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_nt16(uint4* dst, uint4 a) {
+  const u32x4 v = {a.x, a.y, a.z, a.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
+}
+
 constexpr int kHdUnitsPerThread = 1;  // row-blocks per thread of k_quantize_headdim
 
 // One lane owns one 32-channel block of one row (d/32 lanes per row, in the
@@ -83,7 +94,7 @@ __global__ __launch_bounds__(256) void k_quantize_headdim(
     // the exact division by 2^e happens inside the convert
     const uint4 packed = block_codes(v, e);
     if (unit[it] < total_units) {
-      reinterpret_cast<uint4*>(codes)[unit[it]] = packed;
+      store_nt16(reinterpret_cast<uint4*>(codes) + unit[it], packed);
       scales[unit[it]] = (uint8_t)(e + 127);
     }
   }
