@@ -20,7 +20,10 @@
  *     between calls.  Calls are thread-safe.
  *   - Streams: work is enqueued on `stream` (0 = the null stream) and returns
  *     without synchronizing; results are valid once the stream has reached
- *     that point.
+ *     that point.  Kernels run on the calling thread's current HIP device:
+ *     every pointer, and the stream, must belong to that device.  The library
+ *     cannot check this; memory of another device or host memory makes the
+ *     kernels fault.
  *   - Errors: every argument is validated before anything is enqueued; on an
  *     error nothing is written and nothing is launched.  A launch failure
  *     after validation returns MXATTN_ERR_HIP.
