@@ -4,8 +4,8 @@
 One step is the whole hot path on the Wan-like video self-attention shape
 (B=1, H=40, N=32760, d=128, bf16 inputs already in HBM):
   rotate + UOS-quantize Q, rotate + UOS-quantize K, UOS-quantize V along
-  tokens, fused forward (scaled-FP4 QK^T, online softmax with PNQ,
-  scaled-FP4 PV).
+  tokens (one mxattn_rotate_quantize_qkv launch), fused forward (scaled-FP4
+  QK^T, online softmax with PNQ, scaled-FP4 PV).
 
 Prints one JSON line.  `value` is whole-step throughput in TFLOPS, counting
 4*B*H*N^2*d algorithmic flops (2*d per (query, key) pair for QK^T and as many
@@ -16,10 +16,14 @@ plain CPU oracle on a bounded sample of the same workload.  `accuracy` gives
 the error of the output against fp32 softmax attention on the unquantized
 inputs (PyTorch on the GPU, sampled rows, outside the timed region).
 
-With --fused-q the step quantizes K and V and runs the forward entry point
-that rotates and quantizes Q in its own prologue (no Q^ buffer).
+With --separate-quantize the three tensors are quantized by three
+mxattn_rotate_quantize launches, and the JSON line adds per-launch rates for K
+and V.  With --fused-q the step quantizes K and V (two launches) and runs the
+forward entry point that rotates and quantizes Q in its own prologue (no Q^
+buffer).
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--fused-q] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--separate-quantize] [--fused-q]
+                    [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -159,6 +163,9 @@ def main():
     ap.add_argument("--workload", type=int, default=2)
     ap.add_argument("--fused-q", action="store_true",
                     help="rotate and quantize Q inside the forward (mxattn_forward_fused_q)")
+    ap.add_argument("--separate-quantize", action="store_true",
+                    help="quantize Q, K and V with three mxattn_rotate_quantize launches instead of one "
+                         "mxattn_rotate_quantize_qkv launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run three plain device-to-device copies of BYTES bytes and exit "
@@ -220,20 +227,26 @@ def main():
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
     # events (on the launch stream) around the step's parts: e[0] start,
-    # e[1] after Q's quantizer, e[2] after K's, e[3] after V's, e[4] after the
-    # forward
+    # e[1] after Q's quantizer, e[2] after K's, e[3] after V's (with the
+    # single Q, K, V launch e[1] = e[2] = e[0] and e[3] follows that launch),
+    # e[4] after the forward
+    separate = args.fused_q or args.separate_quantize
+
     def step(record=None):
         e = [ev() for _ in range(5)] if record is not None else None
         if e:
             e[0].record(stream)
-        if not args.fused_q:
-            mx.rotate_quantize(dev["q"], mx.AXIS_HEAD_DIM, rotate=True, out=qm)
-        if e:
-            e[1].record(stream)
-        mx.rotate_quantize(dev["k"], mx.AXIS_HEAD_DIM, rotate=True, out=km)
-        if e:
-            e[2].record(stream)
-        mx.rotate_quantize(dev["v"], mx.AXIS_TOKEN, rotate=False, out=vm)
+        if not separate:
+            mx.rotate_quantize_qkv(dev["q"], dev["k"], dev["v"], rotate=True, out=(qm, km, vm))
+        else:
+            if not args.fused_q:
+                mx.rotate_quantize(dev["q"], mx.AXIS_HEAD_DIM, rotate=True, out=qm)
+            if e:
+                e[1].record(stream)
+            mx.rotate_quantize(dev["k"], mx.AXIS_HEAD_DIM, rotate=True, out=km)
+            if e:
+                e[2].record(stream)
+            mx.rotate_quantize(dev["v"], mx.AXIS_TOKEN, rotate=False, out=vm)
         if e:
             e[3].record(stream)
         if args.fused_q:
@@ -255,8 +268,9 @@ def main():
     wall = time.perf_counter() - t0
 
     quant_ms = sum(e[0].elapsed_time(e[3]) for e in events) / len(events)
-    k_ms = sum(e[1].elapsed_time(e[2]) for e in events) / len(events)  # K's rotate + quantize
-    v_ms = sum(e[2].elapsed_time(e[3]) for e in events) / len(events)  # V's quantize
+    if separate:
+        k_ms = sum(e[1].elapsed_time(e[2]) for e in events) / len(events)  # K's rotate + quantize
+        v_ms = sum(e[2].elapsed_time(e[3]) for e in events) / len(events)  # V's quantize
     fwd_ms = sum(e[3].elapsed_time(e[4]) for e in events) / len(events)
     ms_per_step = wall * 1000.0 / args.steps
     flops = w.flops()
@@ -285,8 +299,11 @@ def main():
         "config": {"workload": f"{w.name}: {w.describe()}, one step = " +
                                ("rotate+quantize K; quantize V; fused PNQ forward with Q rotated and "
                                 "quantized in its prologue" if args.fused_q else
-                                "rotate+quantize Q, K; quantize V; fused PNQ forward"),
+                                "rotate+quantize Q, K and quantize V (three launches); fused PNQ forward"
+                                if separate else
+                                "rotate+quantize Q, K and quantize V (one launch); fused PNQ forward"),
                    "B": B, "H": H, "N": N, "d": d, "fused_q": bool(args.fused_q),
+                   "quantizer_launches": (2 if args.fused_q else 3) if separate else 1,
                    "causal": w.causal, "kv_tile": mx.forward_kv_tile(d, w.causal),
                    **({"Nk": Nk} if Nk != N else {})},
         "forward": {"ms": round(fwd_ms, 4), "tflops": round(fwd_tflops, 2),
@@ -294,10 +311,10 @@ def main():
         "quantizer": {"ms": round(quant_ms, 4), "gb_per_s": round(quant_gbs, 1),
                       "frac_hbm_peak": round(quant_gbs / HBM_PEAK_GBS, 4),
                       "bytes": quant_bytes,
-                      # one launch each: K's rotate+quantize (head-dim blocks) and
-                      # V's quantize (token blocks), event-timed on the stream
-                      "rotate_quantize_k": per_launch(k_ms, B * H * Nk * d),
-                      "quantize_v": per_launch(v_ms, B * H * Nk * d)},
+                      # separate launches: K's rotate+quantize (head-dim blocks)
+                      # and V's quantize (token blocks), event-timed on the stream
+                      **({"rotate_quantize_k": per_launch(k_ms, B * H * Nk * d),
+                          "quantize_v": per_launch(v_ms, B * H * Nk * d)} if separate else {})},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
                      "traffic": measured_traffic(flops) if args.workload == 2 and not args.fused_q else None},

@@ -168,6 +168,28 @@ mxattn_status mxattn_rotate_quantize_q(const void* x, int32_t dtype, mxattn_shap
                                        const int64_t* strides, int32_t axis, int32_t rotate,
                                        double q_max, mxattn_mx_tensor* out, hipStream_t stream);
 
+/* Q, K and V of one attention call quantized in a single launch (Alg. 2's
+ * preprocessing of all three inputs): Q and K along the head dimension,
+ * rotated first if `rotate`, V along tokens, all with `rule`.  The outputs
+ * equal those of three mxattn_rotate_quantize calls bit for bit; one launch
+ * saves the two kernel boundaries between them.
+ *   q, k, v    16-bit device inputs, one dtype
+ *   q_shape    [B, H, Nq, d]; kv_shape [B, H, Nk, d] for K and V (same B, H,
+ *              d as Q, else MXATTN_ERR_MISMATCH)
+ *   q_strides, k_strides, v_strides   as in mxattn_rotate_quantize
+ *   rotate     0 or 1 (Q and K)
+ *   rule       MXATTN_SCALE_UOS or MXATTN_SCALE_OCP (else MXATTN_ERR_ENUM)
+ *   q_out, k_out, v_out   host descriptors with caller buffers, as `out` of
+ *              mxattn_rotate_quantize; the call fills their shape, axis,
+ *              rule and rotated fields
+ * Errors: those of mxattn_rotate_quantize for each tensor, then
+ * MXATTN_ERR_ENUM and MXATTN_ERR_MISMATCH; nothing is enqueued on an error. */
+mxattn_status mxattn_rotate_quantize_qkv(const void* q, const void* k, const void* v, int32_t dtype,
+                                         mxattn_shape q_shape, mxattn_shape kv_shape, const int64_t* q_strides,
+                                         const int64_t* k_strides, const int64_t* v_strides, int32_t rotate,
+                                         int32_t rule, mxattn_mx_tensor* q_out, mxattn_mx_tensor* k_out,
+                                         mxattn_mx_tensor* v_out, hipStream_t stream);
+
 /* Workspace needed by mxattn_scale_sweep for `shape`, `axis` and n_q
  * boundaries.  0 for an invalid shape, axis or count. */
 size_t mxattn_scale_sweep_workspace_bytes(mxattn_shape shape, int32_t axis, int32_t n_q);

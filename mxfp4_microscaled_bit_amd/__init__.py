@@ -32,6 +32,7 @@ EXPORTED = (
     "mxattn_forward_kv_tile",
     "mxattn_rotate_quantize",
     "mxattn_rotate_quantize_q",
+    "mxattn_rotate_quantize_qkv",
     "mxattn_scale_sweep_workspace_bytes",
     "mxattn_scale_sweep",
     "mxattn_forward",
@@ -85,6 +86,10 @@ def lib():
     L.mxattn_rotate_quantize_q.restype = i32
     L.mxattn_rotate_quantize_q.argtypes = [vp, i32, Shape, vp, i32, i32, ctypes.c_double,
                                            ctypes.POINTER(MXTensorDesc), vp]
+    L.mxattn_rotate_quantize_qkv.restype = i32
+    L.mxattn_rotate_quantize_qkv.argtypes = [vp, vp, vp, i32, Shape, Shape, vp, vp, vp, i32, i32,
+                                             ctypes.POINTER(MXTensorDesc), ctypes.POINTER(MXTensorDesc),
+                                             ctypes.POINTER(MXTensorDesc), vp]
     L.mxattn_scale_sweep_workspace_bytes.restype = sz
     L.mxattn_scale_sweep_workspace_bytes.argtypes = [Shape, i32, i32]
     L.mxattn_scale_sweep.restype = i32
@@ -250,6 +255,40 @@ def rotate_quantize_q(x: torch.Tensor, q_max: float, axis: int = AXIS_HEAD_DIM, 
                                               _strides(x), axis, int(bool(rotate)), float(q_max),
                                               ctypes.byref(desc), _stream(stream, dev)), "mxattn_rotate_quantize_q")
     out.shape, out.axis, out.rule, out.rotated = (B, H, N, d), axis, SCALE_CEIL_Q, int(bool(rotate))
+    return out
+
+
+def rotate_quantize_qkv(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rotate: bool = True,
+                        rule: int = SCALE_UOS, out: tuple | None = None, stream=None) -> tuple:
+    """mxattn_rotate_quantize_qkv: Q and K along d (rotated if `rotate`), V along
+    tokens, in one launch; returns the three MXTensors (Q^, K^, V^)."""
+    if q.dtype != k.dtype or q.dtype != v.dtype:
+        raise TypeError("q, k and v must share one dtype")
+    if k.shape != v.shape:
+        raise ValueError("k and v must share a shape")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    dev = _device(q, k, v)
+    if out is None:
+        out = (MXTensor.empty(B, H, Nq, d, AXIS_HEAD_DIM, device=dev),
+               MXTensor.empty(B, H, Nk, d, AXIS_HEAD_DIM, device=dev),
+               MXTensor.empty(B, H, Nk, d, AXIS_TOKEN, device=dev))
+    oq, ok, ov = out
+    oq.shape, oq.axis = (B, H, Nq, d), AXIS_HEAD_DIM
+    ok.shape, ok.axis = (B, H, Nk, d), AXIS_HEAD_DIM
+    ov.shape, ov.axis = (B, H, Nk, d), AXIS_TOKEN
+    _device(q, k, v, oq.codes, oq.scales, ok.codes, ok.scales, ov.codes, ov.scales)
+    dq, dk, dv = oq.desc(), ok.desc(), ov.desc()
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_rotate_quantize_qkv(
+            ctypes.c_void_p(q.data_ptr()), ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()),
+            _dtype_enum(q), _shape(B, H, Nq, d), _shape(B, H, Nk, d), _strides(q), _strides(k), _strides(v),
+            int(bool(rotate)), rule, ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv), _stream(stream, dev)),
+            "mxattn_rotate_quantize_qkv")
+    for o in out:
+        o.rule = rule
+    oq.rotated = ok.rotated = int(bool(rotate))
+    ov.rotated = 0
     return out
 
 

@@ -83,9 +83,11 @@ uint32_t boundary_bits(double q) {
   return b;
 }
 
-mxattn_status quantize_common(const void* x, int32_t dtype, mxattn_shape shape, const int64_t* strides,
-                              int32_t axis, int32_t rotate, int32_t rule, uint32_t qbits,
-                              mxattn_mx_tensor* out, hipStream_t stream) {
+// validation and arguments of one quantizer tensor; launches nothing and
+// writes nothing
+mxattn_status prepare_quantize(const void* x, int32_t dtype, mxattn_shape shape, const int64_t* strides,
+                               int32_t axis, int32_t rotate, int32_t rule, uint32_t qbits,
+                               const mxattn_mx_tensor* out, QuantArgs& a) {
   if (!x || !out || !out->codes || !out->scales) return MXATTN_ERR_NULL;
   if (dtype != MXATTN_BF16 && dtype != MXATTN_FP16) return MXATTN_ERR_DTYPE;
   if (axis != MXATTN_AXIS_HEAD_DIM && axis != MXATTN_AXIS_TOKEN) return MXATTN_ERR_ENUM;
@@ -98,7 +100,6 @@ mxattn_status quantize_common(const void* x, int32_t dtype, mxattn_shape shape, 
   if (st != MXATTN_OK) return st;
   if (!aligned16(x) || !aligned16(out->codes) || !aligned16(out->scales)) return MXATTN_ERR_ALIGN;
 
-  QuantArgs a;
   a.x = x;
   a.dtype = dtype;
   a.B = shape.B; a.H = shape.H; a.N = shape.N; a.d = shape.d;
@@ -108,10 +109,23 @@ mxattn_status quantize_common(const void* x, int32_t dtype, mxattn_shape shape, 
   a.qbits = qbits;
   a.codes = out->codes;
   a.scales = out->scales;
+  return MXATTN_OK;
+}
+
+void describe(mxattn_mx_tensor* out, const mxattn_shape& shape, int32_t axis, int32_t rule, int32_t rotate) {
   out->shape = shape;
   out->axis = axis;
   out->rule = rule;
   out->rotated = rotate;
+}
+
+mxattn_status quantize_common(const void* x, int32_t dtype, mxattn_shape shape, const int64_t* strides,
+                              int32_t axis, int32_t rotate, int32_t rule, uint32_t qbits,
+                              mxattn_mx_tensor* out, hipStream_t stream) {
+  QuantArgs a;
+  const mxattn_status st = prepare_quantize(x, dtype, shape, strides, axis, rotate, rule, qbits, out, a);
+  if (st != MXATTN_OK) return st;
+  describe(out, shape, axis, rule, rotate);
   return hip_status(axis == MXATTN_AXIS_HEAD_DIM ? launch_quantize_headdim(a, stream)
                                                  : launch_quantize_tokens(a, stream));
 }
@@ -200,6 +214,28 @@ mxattn_status mxattn_rotate_quantize_q(const void* x, int32_t dtype, mxattn_shap
     return MXATTN_ERR_ENUM;
   return quantize_common(x, dtype, shape, strides, axis, rotate, MXATTN_SCALE_CEIL_Q, boundary_bits(q_max), out,
                          stream);
+}
+
+mxattn_status mxattn_rotate_quantize_qkv(const void* q, const void* k, const void* v, int32_t dtype,
+                                         mxattn_shape q_shape, mxattn_shape kv_shape, const int64_t* q_strides,
+                                         const int64_t* k_strides, const int64_t* v_strides, int32_t rotate,
+                                         int32_t rule, mxattn_mx_tensor* q_out, mxattn_mx_tensor* k_out,
+                                         mxattn_mx_tensor* v_out, hipStream_t stream) {
+  if (!q_out || !k_out || !v_out) return MXATTN_ERR_NULL;
+  QuantArgs aq, ak, av;
+  mxattn_status st =
+      prepare_quantize(q, dtype, q_shape, q_strides, MXATTN_AXIS_HEAD_DIM, rotate, rule, 0u, q_out, aq);
+  if (st != MXATTN_OK) return st;
+  st = prepare_quantize(k, dtype, kv_shape, k_strides, MXATTN_AXIS_HEAD_DIM, rotate, rule, 0u, k_out, ak);
+  if (st != MXATTN_OK) return st;
+  st = prepare_quantize(v, dtype, kv_shape, v_strides, MXATTN_AXIS_TOKEN, 0, rule, 0u, v_out, av);
+  if (st != MXATTN_OK) return st;
+  if (rule != MXATTN_SCALE_UOS && rule != MXATTN_SCALE_OCP) return MXATTN_ERR_ENUM;
+  if (q_shape.B != kv_shape.B || q_shape.H != kv_shape.H || q_shape.d != kv_shape.d) return MXATTN_ERR_MISMATCH;
+  describe(q_out, q_shape, MXATTN_AXIS_HEAD_DIM, rule, rotate);
+  describe(k_out, kv_shape, MXATTN_AXIS_HEAD_DIM, rule, rotate);
+  describe(v_out, kv_shape, MXATTN_AXIS_TOKEN, rule, 0);
+  return hip_status(launch_quantize_qkv(aq, ak, av, stream));
 }
 
 size_t mxattn_scale_sweep_workspace_bytes(mxattn_shape shape, int32_t axis, int32_t n_q) {

@@ -26,6 +26,9 @@ struct QuantArgs {
 
 hipError_t launch_quantize_headdim(const QuantArgs& a, hipStream_t stream);
 hipError_t launch_quantize_tokens(const QuantArgs& a, hipStream_t stream);
+// Q and K along d (rotated if q.rotate), V along tokens, in one launch; the
+// three share dtype, d and rule (UOS or OCP)
+hipError_t launch_quantize_qkv(const QuantArgs& q, const QuantArgs& k, const QuantArgs& v, hipStream_t stream);
 
 constexpr int kSweepMax = 48;  // boundaries per sweep call
 

@@ -8,6 +8,8 @@
 //     tokens of one channel per block (Alg. 2, with the block axis that
 //     the PV product contracts over, as the MatX leaky-quantization page
 //     explains).
+//   k_quantize_qkv: the two above for Q, K and V of one attention call in a
+//     single launch.
 //   k_sweep_headdim / k_sweep_tokens + k_sweep_reduce: the per-head squared
 //     quantization error of the same blocks for a list of ceiling-rule
 //     boundaries q (the Q_max sweep of Sec. 5.5.1, Table 4; Eq. 13).
@@ -47,18 +49,29 @@ __device__ __forceinline__ void store_nt16(uint4* dst, uint4 a) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst));
 }
 
-constexpr int kHdUnitsPerThread = 1;  // row-blocks per thread of k_quantize_headdim
+constexpr int kHdUnitsPerThread = 1;  // row-blocks per thread of the head-dim quantizer
 
-// One lane owns one 32-channel block of one row (d/32 lanes per row, in the
-// same quad), so the first five butterfly stages stay in registers and the
-// remaining one (d=64) or two (d=128) cross lanes through DPP.  Each thread
-// handles one row-block (64 bytes in four 16-byte loads); measured on the
-// Wan-like tensors this beats two or four blocks per thread (more
-// workgroups in flight rather than more loads per lane).
+// One tensor of a quantizer launch: 16-bit input [B, H, N, d] with element
+// strides, and its MXFP4 codes and scales.  `total` counts the work units:
+// row-blocks (B H Np d/32) along d, 32-token blocks (B H Np/32) along tokens.
+struct QTensor {
+  const uint16_t* x;
+  int H, N, Np;
+  int64_t sB, sH, sN;
+  int64_t total;
+  uint8_t* codes;
+  uint8_t* scales;
+};
+
+// Head-dimension quantizer, workgroup `group` of tensor t.  One lane owns one
+// 32-channel block of one row (d/32 lanes per row, in the same quad), so the
+// first five butterfly stages stay in registers and the remaining one (d=64)
+// or two (d=128) cross lanes through DPP.  Each thread handles one row-block
+// (64 bytes in four 16-byte loads); measured on the Wan-like tensors this
+// beats two or four blocks per thread (more workgroups in flight rather than
+// more loads per lane).
 template <int D, int DTYPE, bool ROTATE, int RULE>
-__global__ __launch_bounds__(256) void k_quantize_headdim(
-    const uint16_t* __restrict__ x, int H, int N, int Np, int64_t sB, int64_t sH, int64_t sN,
-    int64_t total_units, uint32_t qb, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+__device__ __forceinline__ void headdim_group(const QTensor& t, uint32_t qb, int64_t group) {
   constexpr int BPR = D / 32;  // blocks (lanes) per row
   static_assert(D == 64 || D == 128, "head dim");
 
@@ -67,17 +80,17 @@ __global__ __launch_bounds__(256) void k_quantize_headdim(
   int64_t unit[QU];
 #pragma unroll
   for (int it = 0; it < QU; ++it) {
-    unit[it] = (int64_t)blockIdx.x * 256 * QU + it * 256 + threadIdx.x;
+    unit[it] = group * 256 * QU + it * 256 + threadIdx.x;
     const int64_t row = unit[it] / BPR;
     const int blk = (int)(unit[it] % BPR);
-    const int64_t bh = row / Np;
-    const int n = (int)(row % Np);
-    const bool live = unit[it] < total_units && n < N;
+    const int64_t bh = row / t.Np;
+    const int n = (int)(row % t.Np);
+    const bool live = unit[it] < t.total && n < t.N;
 #pragma unroll
     for (int k = 0; k < 4; ++k) raw[it][k] = make_uint4(0, 0, 0, 0);
     if (live) {
-      const int64_t b = bh / H, h = bh % H;
-      const uint4* p = reinterpret_cast<const uint4*>(x + b * sB + h * sH + (int64_t)n * sN + 32 * blk);
+      const int64_t b = bh / t.H, h = bh % t.H;
+      const uint4* p = reinterpret_cast<const uint4*>(t.x + b * t.sB + h * t.sH + (int64_t)n * t.sN + 32 * blk);
 #pragma unroll
       for (int k = 0; k < 4; ++k) raw[it][k] = p[k];
     }
@@ -93,30 +106,32 @@ __global__ __launch_bounds__(256) void k_quantize_headdim(
     const int e = scale_exponent<RULE>(M, qb);
     // the exact division by 2^e happens inside the convert
     const uint4 packed = block_codes(v, e);
-    if (unit[it] < total_units) {
-      store_nt16(reinterpret_cast<uint4*>(codes) + unit[it], packed);
-      scales[unit[it]] = (uint8_t)(e + 127);
+    if (unit[it] < t.total) {
+      store_nt16(reinterpret_cast<uint4*>(t.codes) + unit[it], packed);
+      t.scales[unit[it]] = (uint8_t)(e + 127);
     }
   }
 }
 
-// One lane owns two adjacent channels of one 32-token block: it reads the 32
-// tokens of its channel pair (each wave-wide load is one contiguous row of the
-// block), so both block maxima are lane-local, and writes 2 x 16 code bytes
-// and 2 scale bytes contiguously.
+// Token-axis quantizer, workgroup `group` of tensor t.  One lane owns two
+// adjacent channels of one 32-token block: it reads the 32 tokens of its
+// channel pair (each wave-wide load is one contiguous row of the block), so
+// both block maxima are lane-local, and writes 2 x 16 code bytes and 2 scale
+// bytes contiguously.
 template <int D, int DTYPE, int RULE>
-__global__ __launch_bounds__(256) void k_quantize_tokens(
-    const uint16_t* __restrict__ x, int H, int N, int NBp, int64_t sB, int64_t sH, int64_t sN,
-    int64_t total_blocks, uint32_t qb, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+__device__ __forceinline__ void tokens_group(const QTensor& t, uint32_t qb, int64_t group) {
   constexpr int LPB = D / 2;  // lanes per token block
-  const int64_t gl = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t gl = group * 256 + threadIdx.x;
   const int64_t gblk = gl / LPB;
   const int cp = (int)(gl % LPB);
-  if (gblk >= total_blocks) return;
+  if (gblk >= t.total) return;
+  const int NBp = t.Np / 32;
   const int64_t bh = gblk / NBp;
   const int kb = (int)(gblk % NBp);
-  const int64_t b = bh / H, h = bh % H;
-  const uint16_t* base = x + b * sB + h * sH + (int64_t)(32 * kb) * sN + 2 * cp;
+  const int64_t b = bh / t.H, h = bh % t.H;
+  const int N = t.N;
+  const int64_t sN = t.sN;
+  const uint16_t* base = t.x + b * t.sB + h * t.sH + (int64_t)(32 * kb) * sN + 2 * cp;
 
   // all 32 loads are issued before any is used; only a block that crosses N
   // (the last one) takes the guarded path, decided once per wave
@@ -124,33 +139,81 @@ __global__ __launch_bounds__(256) void k_quantize_tokens(
   if (__all(32 * kb + 31 < N)) {
     const uint16_t* pt = base;
 #pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      w[t] = *reinterpret_cast<const uint32_t*>(pt);
+    for (int k = 0; k < 32; ++k) {
+      w[k] = *reinterpret_cast<const uint32_t*>(pt);
       pt += sN;
     }
   } else {
 #pragma unroll
-    for (int t = 0; t < 32; ++t) {
-      const int tc = min(t, max(N - 1 - 32 * kb, 0));  // an in-range row to read from
+    for (int k = 0; k < 32; ++k) {
+      const int tc = min(k, max(N - 1 - 32 * kb, 0));  // an in-range row to read from
       const uint32_t wt = *reinterpret_cast<const uint32_t*>(base + (int64_t)tc * sN);
-      w[t] = (32 * kb + t < N) ? wt : 0u;
+      w[k] = (32 * kb + k < N) ? wt : 0u;
     }
   }
-  float v0[32], v1[32];
+  // block maxima of |x| on the 16-bit patterns: for finite bf16 and fp16
+  // values the magnitude order is the unsigned order of the low 15 bits, so
+  // the maxima need no unpacking (the values are unpacked only for the
+  // codes, which keeps fewer registers live)
+  uint32_t a0 = 0u, a1 = 0u;
 #pragma unroll
-  for (int t = 0; t < 32; ++t) unpack2<DTYPE>(w[t], v0[t], v1[t]);
-  float m0 = 0.0f, m1 = 0.0f;
-#pragma unroll
-  for (int t = 0; t < 32; ++t) {
-    m0 = fmaxf(m0, fabsf(v0[t]));
-    m1 = fmaxf(m1, fabsf(v1[t]));
+  for (int k = 0; k < 32; ++k) {
+    a0 = max(a0, w[k] & 0x7FFFu);
+    a1 = max(a1, (w[k] >> 16) & 0x7FFFu);
   }
+  float m0, m1;
+  unpack2<DTYPE>(a0 | (a1 << 16), m0, m1);
   const int e0 = scale_exponent<RULE>(m0, qb), e1 = scale_exponent<RULE>(m1, qb);
-  uint4* dst = reinterpret_cast<uint4*>(codes + (gblk * D + 2 * cp) * 16);
-  dst[0] = block_codes(v0, e0);
-  dst[1] = block_codes(v1, e1);
-  *reinterpret_cast<uint16_t*>(scales + gblk * D + 2 * cp) =
+  // codes eight tokens at a time, as block_codes() forms them: the convert
+  // divides by 2^e; at the clamp e = -127 the values are first moved up
+  // exactly by 2^127 and converted with unit scale
+  const bool tiny = (e0 < -126) | (e1 < -126);
+  const int k0 = e0 < -126 ? 127 : 0, k1 = e1 < -126 ? 127 : 0;
+  const float s0 = pow2f(e0 < -126 ? 0 : e0), s1 = pow2f(e1 < -126 ? 0 : e1);
+  uint32_t c0[4], c1[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    float lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) unpack2<DTYPE>(w[8 * c + i], lo[i], hi[i]);
+    if (tiny) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lo[i] = __builtin_amdgcn_ldexpf(lo[i], k0);
+        hi[i] = __builtin_amdgcn_ldexpf(hi[i], k1);
+      }
+    }
+    c0[c] = cvt8(lo, s0);
+    c1[c] = cvt8(hi, s1);
+  }
+  uint4* dst = reinterpret_cast<uint4*>(t.codes + (gblk * D + 2 * cp) * 16);
+  dst[0] = make_uint4(c0[0], c0[1], c0[2], c0[3]);
+  dst[1] = make_uint4(c1[0], c1[1], c1[2], c1[3]);
+  *reinterpret_cast<uint16_t*>(t.scales + gblk * D + 2 * cp) =
       (uint16_t)((uint32_t)(e0 + 127) | ((uint32_t)(e1 + 127) << 8));
+}
+
+template <int D, int DTYPE, bool ROTATE, int RULE>
+__global__ __launch_bounds__(256) void k_quantize_headdim(QTensor t, uint32_t qb) {
+  headdim_group<D, DTYPE, ROTATE, RULE>(t, qb, blockIdx.x);
+}
+
+template <int D, int DTYPE, int RULE>
+__global__ __launch_bounds__(256) void k_quantize_tokens(QTensor t, uint32_t qb) {
+  tokens_group<D, DTYPE, RULE>(t, qb, blockIdx.x);
+}
+
+// Q, K and V of one attention call in one launch: workgroups [0, gq) quantize
+// Q and [gq, gq + gk) K along d (rotated if ROTATE), the rest V along tokens.
+// One launch instead of three saves two kernel boundaries, where the GPU
+// drains one grid before the next one fills it.
+template <int D, int DTYPE, bool ROTATE, int RULE>
+__global__ __launch_bounds__(256) void k_quantize_qkv(QTensor q, QTensor k, QTensor v, int64_t gq, int64_t gk,
+                                                      uint32_t qb) {
+  const int64_t g = blockIdx.x;
+  if (g < gq) headdim_group<D, DTYPE, ROTATE, RULE>(q, qb, g);
+  else if (g < gq + gk) headdim_group<D, DTYPE, ROTATE, RULE>(k, qb, g - gq);
+  else tokens_group<D, DTYPE, RULE>(v, qb, g - gq - gk);
 }
 
 // ---------------------------------------------------------------------------
@@ -346,27 +409,63 @@ hipError_t launch_sweep_typed(const SweepArgs& a, const SweepQ& sq, hipStream_t 
   return hipGetLastError();
 }
 
+QTensor headdim_tensor(const QuantArgs& a) {
+  QTensor t;
+  t.x = static_cast<const uint16_t*>(a.x);
+  t.H = a.H;
+  t.N = a.N;
+  t.Np = (int)padded_tokens(a.N);
+  t.sB = a.sB; t.sH = a.sH; t.sN = a.sN;
+  t.total = (int64_t)a.B * a.H * t.Np * (a.d / 32);
+  t.codes = a.codes;
+  t.scales = a.scales;
+  return t;
+}
+
+QTensor tokens_tensor(const QuantArgs& a) {
+  QTensor t = headdim_tensor(a);
+  t.total = (int64_t)a.B * a.H * (t.Np / 32);
+  return t;
+}
+
+int64_t headdim_groups(const QTensor& t) { return (t.total + 256 * kHdUnitsPerThread - 1) / (256 * kHdUnitsPerThread); }
+template <int D>
+int64_t tokens_groups(const QTensor& t) { return (t.total * (D / 2) + 255) / 256; }
+
 template <int D, int DTYPE, bool ROTATE, int RULE>
 hipError_t launch_hd(const QuantArgs& a, hipStream_t stream) {
-  const int64_t Np = padded_tokens(a.N);
-  const int64_t total = (int64_t)a.B * a.H * Np * (D / 32);
-  const int64_t grid = (total + 256 * kHdUnitsPerThread - 1) / (256 * kHdUnitsPerThread);
-  hipLaunchKernelGGL((k_quantize_headdim<D, DTYPE, ROTATE, RULE>), dim3((unsigned)grid), dim3(256), 0,
-                     stream, static_cast<const uint16_t*>(a.x), a.H, a.N, (int)Np, a.sB, a.sH, a.sN,
-                     total, a.qbits, a.codes, a.scales);
+  const QTensor t = headdim_tensor(a);
+  hipLaunchKernelGGL((k_quantize_headdim<D, DTYPE, ROTATE, RULE>), dim3((unsigned)headdim_groups(t)), dim3(256), 0,
+                     stream, t, a.qbits);
   return hipGetLastError();
 }
 
 template <int D, int DTYPE, int RULE>
 hipError_t launch_tok(const QuantArgs& a, hipStream_t stream) {
-  const int64_t NBp = padded_tokens(a.N) / 32;
-  const int64_t total_blocks = (int64_t)a.B * a.H * NBp;
-  const int64_t lanes = total_blocks * (D / 2);
-  const int64_t grid = (lanes + 255) / 256;
-  hipLaunchKernelGGL((k_quantize_tokens<D, DTYPE, RULE>), dim3((unsigned)grid), dim3(256), 0, stream,
-                     static_cast<const uint16_t*>(a.x), a.H, a.N, (int)NBp, a.sB, a.sH, a.sN,
-                     total_blocks, a.qbits, a.codes, a.scales);
+  const QTensor t = tokens_tensor(a);
+  hipLaunchKernelGGL((k_quantize_tokens<D, DTYPE, RULE>), dim3((unsigned)tokens_groups<D>(t)), dim3(256), 0, stream,
+                     t, a.qbits);
   return hipGetLastError();
+}
+
+template <int D, int DTYPE, bool ROTATE, int RULE>
+hipError_t launch_qkv(const QuantArgs& q, const QuantArgs& k, const QuantArgs& v, hipStream_t stream) {
+  const QTensor tq = headdim_tensor(q), tk = headdim_tensor(k), tv = tokens_tensor(v);
+  const int64_t gq = headdim_groups(tq), gk = headdim_groups(tk), gv = tokens_groups<D>(tv);
+  hipLaunchKernelGGL((k_quantize_qkv<D, DTYPE, ROTATE, RULE>), dim3((unsigned)(gq + gk + gv)), dim3(256), 0, stream,
+                     tq, tk, tv, gq, gk, q.qbits);
+  return hipGetLastError();
+}
+
+template <int D, int DTYPE, bool ROTATE>
+hipError_t dispatch_qkv_rule(const QuantArgs& q, const QuantArgs& k, const QuantArgs& v, hipStream_t s) {
+  if (q.rule == kRuleOcp) return launch_qkv<D, DTYPE, ROTATE, kRuleOcp>(q, k, v, s);
+  return launch_qkv<D, DTYPE, ROTATE, kRuleUos>(q, k, v, s);
+}
+
+template <int D, int DTYPE>
+hipError_t dispatch_qkv(const QuantArgs& q, const QuantArgs& k, const QuantArgs& v, hipStream_t s) {
+  return q.rotate ? dispatch_qkv_rule<D, DTYPE, true>(q, k, v, s) : dispatch_qkv_rule<D, DTYPE, false>(q, k, v, s);
 }
 
 template <int D, int DTYPE, bool ROTATE>
@@ -398,6 +497,11 @@ hipError_t launch_quantize_headdim(const QuantArgs& a, hipStream_t stream) {
 hipError_t launch_quantize_tokens(const QuantArgs& a, hipStream_t stream) {
   if (a.d == 128) return a.dtype == 1 ? dispatch_tok_rule<128, 1>(a, stream) : dispatch_tok_rule<128, 0>(a, stream);
   return a.dtype == 1 ? dispatch_tok_rule<64, 1>(a, stream) : dispatch_tok_rule<64, 0>(a, stream);
+}
+
+hipError_t launch_quantize_qkv(const QuantArgs& q, const QuantArgs& k, const QuantArgs& v, hipStream_t stream) {
+  if (q.d == 128) return q.dtype == 1 ? dispatch_qkv<128, 1>(q, k, v, stream) : dispatch_qkv<128, 0>(q, k, v, stream);
+  return q.dtype == 1 ? dispatch_qkv<64, 1>(q, k, v, stream) : dispatch_qkv<64, 0>(q, k, v, stream);
 }
 
 int sweep_chunks(int axis, int N, int d) {

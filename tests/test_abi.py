@@ -258,3 +258,37 @@ def test_binding_buffer_lengths():
         mx._buffer(torch.zeros(15, dtype=torch.float32), 64, "out")
     with pytest.raises(ValueError, match="contiguous"):
         mx._buffer(torch.zeros(8, 8)[:, ::2], 16, "out")
+
+
+def test_rotate_quantize_qkv_rejects_bad_arguments_without_writing():
+    """Every case fails validation, so nothing is launched and no descriptor
+    is written."""
+    L = mx.lib()
+
+    def qkv(q=FAKE, k=FAKE, v=FAKE, dtype=mx.BF16, qs=(1, 2, 64, 64), kvs=(1, 2, 64, 64), rotate=1, rule=0,
+            outs=None):
+        if outs is None:
+            outs = [mx.MXTensorDesc(FAKE, FAKE + 4096, mx.Shape(0, 0, 0, 0), 5, 5, 5) for _ in range(3)]
+        st = L.mxattn_rotate_quantize_qkv(q, k, v, dtype, mx.Shape(*qs), mx.Shape(*kvs), None, None, None, rotate,
+                                          rule, *[ctypes.byref(o) if o is not None else None for o in outs], None)
+        return st, outs
+
+    cases = [
+        (dict(q=None), 1),
+        (dict(v=None), 1),
+        (dict(outs=[None, None, None]), 1),
+        (dict(dtype=5), 3),
+        (dict(qs=(1, 2, 64, 96), kvs=(1, 2, 64, 96)), 2),
+        (dict(k=FAKE + 8), 4),
+        (dict(rotate=2), 8),
+        (dict(rule=2), 8),
+        (dict(rule=9), 8),
+        (dict(qs=(1, 3, 64, 64)), 6),
+        (dict(qs=(1, 2, 64, 128)), 6),
+    ]
+    for kwargs, expect in cases:
+        status, outs = qkv(**kwargs)
+        assert status == expect, (kwargs, status)
+        if "outs" not in kwargs:
+            for o in outs:
+                assert (o.axis, o.rule, o.rotated, o.shape.N) == (5, 5, 5, 0)

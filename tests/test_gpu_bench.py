@@ -36,9 +36,17 @@ def test_bench_json_line():
     assert rf["achieved"] == d["forward"]["tflops"]
     q = d["quantizer"]
     assert q["gb_per_s"] > 0 and 0 < q["frac_hbm_peak"] < 1
-    assert q["rotate_quantize_k"]["us"] > 0 and q["quantize_v"]["us"] > 0
+    assert d["config"]["quantizer_launches"] == 1 and "rotate_quantize_k" not in q
     a = d["accuracy"]
     assert -1.0 <= a["mean_row_cosine"] <= 1.0 and a["max_abs"] >= 0
+
+
+@pytest.mark.gpu
+def test_bench_separate_quantizer_launches():
+    d = _run("--workload", "1", "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--separate-quantize")
+    q = d["quantizer"]
+    assert d["config"]["quantizer_launches"] == 3
+    assert q["rotate_quantize_k"]["us"] > 0 and q["quantize_v"]["us"] > 0
 
 
 def test_bench_refuses_more_than_one_gpu():

@@ -187,3 +187,30 @@ def test_binding_rejects_short_buffers_before_launch():
     with pytest.raises(ValueError, match="bytes"):
         mx.p_diagnostics(x, x, out=torch.empty(10, dtype=torch.float32, device="cuda"))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("B,H,Nq,Nk,d,dt,rotate,rule", [
+    (1, 3, 300, 300, 128, torch.bfloat16, True, mx.SCALE_UOS),
+    (2, 2, 129, 4100, 64, torch.float16, True, mx.SCALE_OCP),
+    (1, 2, 1, 33, 128, torch.bfloat16, False, mx.SCALE_UOS),
+    (3, 1, 1000, 77, 64, torch.bfloat16, False, mx.SCALE_OCP),
+])
+def test_qkv_launch_equals_three_calls(B, H, Nq, Nk, d, dt, rotate, rule):
+    """The single Q, K, V launch writes exactly what three separate quantizer
+    calls write, padding included, for contiguous and strided inputs."""
+    say(f"qkv launch: B{B} H{H} Nq{Nq} Nk{Nk} d{d} {dt} rotate={rotate} rule={rule}")
+    g = torch.Generator(device="cpu").manual_seed(Nq * 7 + Nk)
+    q = (torch.randn(B, H, Nq, d, generator=g) * 3).to(dt).cuda()
+    k = (torch.randn(B, H, Nk, d, generator=g) * 0.5).to(dt).cuda()
+    # V as a strided view: every other token of a longer tensor
+    vbig = (torch.randn(B, H, 2 * Nk, d, generator=g) * 20).to(dt).cuda()
+    v = vbig[:, :, ::2]
+    refs = (mx.rotate_quantize(q, mx.AXIS_HEAD_DIM, rotate=rotate, rule=rule),
+            mx.rotate_quantize(k, mx.AXIS_HEAD_DIM, rotate=rotate, rule=rule),
+            mx.rotate_quantize(v, mx.AXIS_TOKEN, rotate=False, rule=rule))
+    outs = mx.rotate_quantize_qkv(q, k, v, rotate=rotate, rule=rule)
+    torch.cuda.synchronize()
+    for name, r, o in zip("qkv", refs, outs):
+        assert torch.equal(r.codes, o.codes), name
+        assert torch.equal(r.scales, o.scales), name
+        assert (o.shape, o.axis, o.rule, o.rotated) == (r.shape, r.axis, r.rule, r.rotated), name
