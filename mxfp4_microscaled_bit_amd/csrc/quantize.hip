@@ -177,6 +177,8 @@ __device__ __forceinline__ void tokens_group(const QTensor& t, uint32_t qb, int6
 #pragma unroll
     for (int i = 0; i < 8; ++i) unpack2<DTYPE>(w[8 * c + i], lo[i], hi[i]);
     if (tiny) {
+      // ldexp by 0 leaves the other channel's values unchanged (binary32
+      // subnormals are kept: these kernels run with denormals enabled)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         lo[i] = __builtin_amdgcn_ldexpf(lo[i], k0);

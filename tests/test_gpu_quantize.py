@@ -214,3 +214,29 @@ def test_qkv_launch_equals_three_calls(B, H, Nq, Nk, d, dt, rotate, rule):
         assert torch.equal(r.codes, o.codes), name
         assert torch.equal(r.scales, o.scales), name
         assert (o.shape, o.axis, o.rule, o.rotated) == (r.shape, r.axis, r.rule, r.rotated), name
+
+
+def test_token_blocks_at_the_exponent_clamp_next_to_subnormal_blocks():
+    """V token blocks whose maximum is tiny enough for the clamp e = -127,
+    beside blocks of the neighbouring channel with e = -126 or -125 that
+    hold subnormal values: both channels of a lane pair go through the
+    clamp path's rescaling, and every code must match the oracle."""
+    say("token quantizer: clamp exponent next to subnormal blocks")
+    N, d = 96, 64
+    rng = np.random.default_rng(11)
+    vals = np.zeros((1, 1, N, d))
+    tiny = 2.0 ** -133 * rng.integers(-40, 41, size=(N, d // 2))   # bf16 subnormals, max < 2^-127
+    small = 2.0 ** -133 * rng.integers(-900, 901, size=(N, d // 2))  # subnormals up to ~2^-123
+    vals[0, 0, :, 0::2] = tiny
+    vals[0, 0, :, 1::2] = small
+    vals[0, 0, 5, 1::4] = 2.0 ** -126 * 7.0  # some neighbour blocks with a normal maximum
+    bits = W.to_bits(vals, W.BF16)
+    for rule in (mx.SCALE_UOS, mx.SCALE_OCP):
+        bc, bs, n = compare_tokens(bits, W.BF16, 1, 1, N, d, rule)
+        assert bc == 0 and bs == 0, rule
+    # the same blocks through the single Q, K, V launch
+    x = to_device(bits, W.BF16)
+    ref = mx.rotate_quantize(x, mx.AXIS_TOKEN, rotate=False)
+    _, _, vm = mx.rotate_quantize_qkv(x, x, x, rotate=False)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.codes, vm.codes) and torch.equal(ref.scales, vm.scales)
