@@ -776,34 +776,21 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
   if constexpr (MODE == kModePnq) l = lsum;
   else if constexpr (MODE == kModeDirect) l = rs.l;
   else l = 1.0f;
-  // The accumulators hold, per lane, 4-float pieces of one query row; a
-  // direct store would give each 128-byte output line 32 bytes per store.
-  // Each 32-channel slice of the wave's 32 x d tile therefore goes through
-  // LDS (rows padded by 16 bytes against bank conflicts) and out as whole
-  // 128-byte row segments, eight lanes per row.
-  constexpr int RB = 32 * 4 + 16;  // staged bytes per row
-  static_assert(4 * 32 * RB <= kLdsBytes<D>, "output staging exceeds the key/value stages");
-  uint8_t* const stg = lds + wave * 32 * RB;
-  const int srow = lane >> 3, scol = 16 * (lane & 7);
-  const int qbase = qt * kBr + 32 * wave;
-  __syncthreads();  // every wave is done with the last key/value tile
+  // Lane (r, g) holds channels 32 ct + 8 j + 4 g + (0..3) of query qi in
+  // accumulator elements 4 j .. 4 j + 3: one 16-byte store each.  (Staging the
+  // tile through LDS into whole 128-byte row segments measured no faster on
+  // the Wan-like shape and 4-5 % slower on the causal and cross-attention
+  // shapes, whose short key loops make the epilogue a larger share.)
+  if (qi < p.Nq) {
+    float* orow = p.out + (bh * p.Nq + qi) * D;
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const v16f& o = acc[ct];
+    for (int ct = 0; ct < NCT; ++ct) {
+      const v16f& o = acc[ct];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<float4*>(stg + r * RB + 4 * (8 * j + 4 * g)) =
-          make_float4(o[4 * j] / l, o[4 * j + 1] / l, o[4 * j + 2] / l, o[4 * j + 3] / l);
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int row = srow + 8 * k;
-      const float4 v = *reinterpret_cast<const float4*>(stg + row * RB + scol);
-      if (qbase + row < p.Nq)
-        *reinterpret_cast<float4*>(reinterpret_cast<uint8_t*>(p.out + (bh * p.Nq + qbase + row) * D + 32 * ct) +
-                                   scol) = v;
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(orow + 32 * ct + 8 * j + 4 * g) =
+            make_float4(o[4 * j] / l, o[4 * j + 1] / l, o[4 * j + 2] / l, o[4 * j + 3] / l);
     }
-    __syncthreads();
   }
   if (g == 0 && qi < p.Nq) {
     if (p.row_stats) {
