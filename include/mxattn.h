@@ -28,6 +28,8 @@
  *     error nothing is written and nothing is launched.  A launch failure
  *     after validation returns MXATTN_ERR_HIP.
  *   - Inputs must be finite.  Outputs for non-finite inputs are unspecified.
+ *   - Output and workspace buffers must not overlap each other or any input
+ *     of the same call (the library cannot check this).
  *   - Alignment: every device pointer must be 16-byte aligned.
  *
  * Layouts
