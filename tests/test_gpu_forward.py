@@ -270,3 +270,62 @@ def test_forward_is_deterministic():
     a, sa = run_forward(dev["q"], dev["k"], dev["v"], False)
     b, sb = run_forward(dev["q"], dev["k"], dev["v"], False)
     assert torch.equal(a, b) and torch.equal(sa, sb)
+
+
+def test_side_stream_gives_the_same_result():
+    """Work enqueued on a caller's non-default stream (default priority) gives
+    the result of the current-stream path; the caller orders the streams with
+    events."""
+    say("forward on a side stream")
+    w = W.WORKLOADS[1]
+    dev = {t: to_device(W.generate(w, t), w.dtype) for t in "qkv"}
+    ref, _ = run_forward(dev["q"], dev["k"], dev["v"], False)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        qm, km, vm = mx.rotate_quantize_qkv(dev["q"], dev["k"], dev["v"], rotate=True, stream=side)
+        out = mx.forward(qm, km, vm, causal=False, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_hip_graph_replays_match_eager():
+    """The path allocates nothing and issues no memsets, so the quantizer and
+    forward launches can be captured in a HIP graph.  Several replays, with
+    eager work and synchronizations between them, each equal the eager
+    result."""
+    say("forward under HIP graph capture")
+    w = W.WORKLOADS[1]
+    dev = {t: to_device(W.generate(w, t), w.dtype) for t in "qkv"}
+    B, H, N, d = w.shape
+    outs = (mx.MXTensor.empty(B, H, N, d, mx.AXIS_HEAD_DIM), mx.MXTensor.empty(B, H, N, d, mx.AXIS_HEAD_DIM),
+            mx.MXTensor.empty(B, H, N, d, mx.AXIS_TOKEN))
+    out = torch.empty((B, H, N, d), dtype=torch.float32, device="cuda")
+    stats = torch.empty((B, H, N, 2), dtype=torch.float32, device="cuda")
+
+    def path():
+        mx.rotate_quantize_qkv(dev["q"], dev["k"], dev["v"], rotate=True, out=outs)
+        mx.forward(*outs, causal=False, out=out, row_stats=stats)
+
+    path()
+    torch.cuda.synchronize()
+    ref, ref_stats = out.clone(), stats.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm up on a side stream before capture
+        path()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        path()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        stats.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref) and torch.equal(stats, ref_stats), rep
+        path()  # eager work between replays
+        torch.cuda.synchronize()
