@@ -75,6 +75,10 @@ static int floor_log2_ratio(double M, double q) {
 }
 
 int oracle_scale_exponent(double M, int rule, double q) {
+  /* outside the precondition (M > 0 finite; q > 0 finite for the *_Q rules)
+   * the searches below would not terminate: return 0 instead */
+  if (!(M > 0.0) || !isfinite(M)) return 0;
+  if ((rule == ORACLE_RULE_CEIL_Q || rule == ORACLE_RULE_FLOOR_Q) && (!(q > 0.0) || !isfinite(q))) return 0;
   switch (rule) {
     case ORACLE_RULE_UOS: /* UOS boundary q* = 29/4 [P1 Eq. 38-39, Alg. 1] */
       return ceil_log2_ratio(M, 7.25);

@@ -63,7 +63,8 @@ double oracle_e2m1_value(int code);
 int oracle_e2m1_project(double y);
 
 /* Shared-scale exponent for block maximum M > 0 under `rule` (q is read by
- * the *_Q rules only).  Returned unclamped. */
+ * the *_Q rules only).  Returned unclamped.  M <= 0, a non-finite M, or (for
+ * the *_Q rules) q <= 0 or non-finite return 0. */
 int oracle_scale_exponent(double M, int rule, double q);
 
 /* oracle_scale_exponent over an array: out[i] for M[i] > 0. */

@@ -825,3 +825,16 @@ def test_diagnostics_decomposition_and_postnorm_row_sums(cid):
     # the sharp workload zeroes many elements; the outlier one saturates some
     if cid == 5:
         assert diag[..., 1].min() < -1e-3
+
+
+def test_scale_exponent_outside_its_precondition_returns_zero():
+    """M > 0 finite (and q > 0 finite for the boundary rules) is the
+    precondition; outside it the exponent search would not terminate, so the
+    oracle returns 0 instead.  Inside it nothing changes (the worked examples
+    above still hold)."""
+    for M in (0.0, -0.0, -1.0, float("inf"), float("nan")):
+        for rule in (oracle.RULE_UOS, oracle.RULE_OCP):
+            assert oracle.scale_exponent(M, rule) == 0
+    assert oracle.scale_exponent(1.0, oracle.RULE_CEIL_Q, 0.0) == 0
+    assert oracle.scale_exponent(1.0, oracle.RULE_CEIL_Q, float("inf")) == 0
+    assert oracle.scale_exponent(14.5, oracle.RULE_UOS) == 1 and oracle.scale_exponent(1.0, oracle.RULE_UOS) == -2
