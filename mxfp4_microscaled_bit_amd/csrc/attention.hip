@@ -520,6 +520,34 @@ __device__ __forceinline__ void q_prologue_quantize(const Params& p, int lane, c
   }
 }
 
+// Deferred PV products.  At d = 64, and under the causal mask, the PV
+// products of a tile's second 64-key half are issued in the next tile, right
+// after its score products, instead of at the end of their own tile (after
+// the last key tile they are issued before the epilogue).  At d = 64 this
+// leaves fewer registers live across the tile boundary (165 instead of 184
+// VGPRs, so three waves fit per SIMD instead of two) and measured 17-19 %
+// faster; under the causal mask it measured 2-4 % faster at d = 128, and
+// 1-2 % slower on the non-causal d = 128 shape, which keeps the original
+// order.  The order of the products on each accumulator is unchanged, so the
+// results are bit-identical.
+template <int D, bool CAUSAL>
+constexpr bool kDeferPV = (D == 64) || CAUSAL;
+
+template <int D>
+struct PendingPV {
+  uint4 vop[D / 32];  // V^ operands of the deferred half
+  uint4 pq;           // its P^ codes (all zero: nothing deferred yet)
+  int vsc, psc;       // its V^ and P^ scale registers
+};
+
+template <int D>
+__device__ __forceinline__ void issue_pending(const PendingPV<D>& pd, v16f (&acc)[D / 32], v4f& accl, uint4 ones,
+                                              int one_sc) {
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct) acc[ct] = mfma32_sel(ct, 0, pd.vop[ct], pd.pq, acc[ct], pd.vsc, pd.psc);
+  accl = mfma16(ones, pd.pq, accl, one_sc, pd.psc);
+}
+
 // One key tile for the wave's 32 queries.  Order: all S products; block and
 // row maxima; P^ of the first 64-key half and its PV products, which run on
 // the matrix cores while P^ of the second half is formed; then the second
@@ -530,7 +558,7 @@ template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
 __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[D / 64],
                                           int qsc, int q, uint4 ones, int one_sc, RowState& rs, v16f (&acc)[D / 32],
                                           v4f& accl, int (&held)[4], int lane, const int (&koff)[D / 64],
-                                          float (&dg)[6], float gamma_f, float inv_gamma_f) {
+                                          float (&dg)[6], float gamma_f, float inv_gamma_f, PendingPV<D>& pend) {
   using L = Lds<D>;
   using F = FwdConsts<D, MODE, RULE>;
   constexpr int NH = D / 64;   // K steps of one S^T sub-tile
@@ -561,10 +589,13 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 
-  // ---- running max, block maxima, alpha
+  // ---- running max, block maxima, alpha (and the deferred PV products of
+  // the previous tile, which must precede this tile's rescale)
+  constexpr bool kDefer = kDeferPV<D, CAUSAL> && MODE != kModeStats && MODE != kModeDiag;
   mask_scores<CAUSAL, MASKED>(s, kt, N, q, g);
   float bmax[2];
   bmax[0] = max32(s[0], s[1]);
+  if constexpr (kDefer) issue_pending<D>(pend, acc, accl, ones, one_sc);
   bmax[1] = max32(s[2], s[3]);
   const float tmax = fmaxf(bmax[0], bmax[1]);
   // this tile's S products and the previous tile's PV products have read
@@ -602,6 +633,10 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
       }
     }
     float lsum = 0.0f;
+    if constexpr (kDefer) {  // scales of the deferred products issued above
+      held[0] = pend.vsc;
+      held[1] = pend.psc;
+    }
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       uint4 vop[NCT];
@@ -612,16 +647,29 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
       float lpart = 0.0f;
       const uint4 pq = quantize_block<D, MODE, RULE>(s[2 * hb], s[2 * hb + 1], bmax[hb], rs, psc, lpart);
       lsum += lpart;
-      __builtin_amdgcn_sched_barrier(0);
+      const int vsc = hb ? (int)vsw.y : (int)vsw.x;
+      if (kDefer && hb == 1) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        acc[ct] = mfma32_sel(ct, 0, vop[ct], pq, acc[ct], hb ? (int)vsw.y : (int)vsw.x, psc);
-      accl = mfma16(ones, pq, accl, one_sc, psc);
-      __builtin_amdgcn_sched_barrier(0);
-      held[2 + hb] = psc;
+        for (int ct = 0; ct < NCT; ++ct) pend.vop[ct] = vop[ct];
+        pend.pq = pq;
+        pend.vsc = vsc;
+        pend.psc = psc;
+      } else {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) acc[ct] = mfma32_sel(ct, 0, vop[ct], pq, acc[ct], vsc, psc);
+        accl = mfma16(ones, pq, accl, one_sc, psc);
+        __builtin_amdgcn_sched_barrier(0);
+        // scale registers of the products issued in this tile
+        if (kDefer) {
+          held[2] = vsc;
+          held[3] = psc;
+        } else {
+          held[hb] = vsc;
+          held[2 + hb] = psc;
+        }
+      }
     }
-    held[0] = (int)vsw.x;
-    held[1] = (int)vsw.y;
     if constexpr (MODE == kModeDirect) rs.l = a * rs.l + pair_sum(lsum);
   }
 }
@@ -689,6 +737,12 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
   for (int ct = 0; ct < NCT; ++ct)
     acc[ct] = v16f{0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   v4f accl = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+  PendingPV<D> pend;  // nothing deferred yet: zero codes add nothing
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) pend.vop[ct] = make_uint4(0u, 0u, 0u, 0u);
+  pend.pq = make_uint4(0u, 0u, 0u, 0u);
+  pend.vsc = 0x7F7F7F7F;
+  pend.psc = 127;
 
   const DmaPlan<D> plan(tid);
   if constexpr (FUSEDQ) {
@@ -729,7 +783,7 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
     codes_dma<D>(p, plan, bh, kn, nxt, tid);
     const ScaleRegs sr = scale_load<D>(p, bh, kn, tid);
     tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, one_sc, rs, acc, accl, held, lane,
-                                            koff, dg, p.gamma_f, p.inv_gamma_f);
+                                            koff, dg, p.gamma_f, p.inv_gamma_f, pend);
     scale_store<D>(sr, nxt, tid);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -737,7 +791,12 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
   // at most one masked tile: the ragged end of the keys or the causal diagonal
   if (nfull < nkt)
     tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, ones, one_sc, rs,
-                                           acc, accl, held, lane, koff, dg, p.gamma_f, p.inv_gamma_f);
+                                           acc, accl, held, lane, koff, dg, p.gamma_f, p.inv_gamma_f, pend);
+  if constexpr (kDeferPV<D, CAUSAL> && MODE != kModeStats && MODE != kModeDiag) {
+    issue_pending<D>(pend, acc, accl, ones, one_sc);  // the last tile's second half
+    held[0] = pend.vsc;
+    held[1] = pend.psc;
+  }
 
   // ---- epilogue
   if constexpr (MODE == kModeStats) {
