@@ -329,3 +329,32 @@ def test_hip_graph_replays_match_eager():
         assert torch.equal(out, ref) and torch.equal(stats, ref_stats), rep
         path()  # eager work between replays
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("p_mode,rule,rotate", [
+    (mx.P_DIRECT, mx.SCALE_OCP, False),
+    (mx.P_DIRECT, mx.SCALE_UOS, True),
+    (mx.P_POSTNORM, mx.SCALE_UOS, True),
+    (mx.P_PNQ, mx.SCALE_OCP, True),
+])
+@pytest.mark.parametrize("d", [64, 128])
+def test_reference_modes_causal_match_oracle(p_mode, rule, rotate, d):
+    """Every placement under the causal mask (the path whose second-half PV
+    products are deferred into the next tile), ragged N, against the oracle."""
+    B, H, N = 2, 2, 300
+    say(f"reference modes causal: d={d} p_mode={p_mode} rule={rule} rotate={rotate}")
+    x = W.custom(B, H, N, d, seed=3 * N + d + p_mode, scale=2.0)
+    dev = {t: to_device(x[t], W.BF16) for t in "qkv"}
+    sums = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    out = mx.quantize_reference_modes(dev["q"], dev["k"], dev["v"], rule=rule, p_mode=p_mode, rotate=rotate,
+                                      causal=True, row_sums=sums)
+    torch.cuda.synchronize()
+    ref = oracle.attention(x["q"], x["k"], x["v"], W.BF16, B, H, N, d, causal=True, rotate=rotate, rule=rule,
+                           p_mode=p_mode, kv_tile=KV_TILE, amb_delta=DELTA)
+    check_output(out.cpu().numpy(), ref, f"causal d={d} mode {p_mode}/{rule}/{rotate}", (N + KV_TILE - 1) // KV_TILE)
+    rs = sums.cpu().numpy()
+    if p_mode == mx.P_PNQ:
+        assert np.abs(rs - 1).max() < 1e-5
+    else:
+        unique = ref["amb"].max(axis=-1) <= 1e-2
+        assert np.allclose(rs[unique], ref["rowsum"][unique], rtol=2e-4, atol=2e-4)
