@@ -549,11 +549,12 @@ __device__ __forceinline__ void issue_pending(const PendingPV<D>& pd, v16f (&acc
 }
 
 // One key tile for the wave's 32 queries.  Order: all S products; block and
-// row maxima; P^ of the first 64-key half and its PV products, which run on
-// the matrix cores while P^ of the second half is formed; then the second
-// half's PV products.  MASKED tiles (the ragged last tile and the causal
-// diagonal) set scores of invisible keys to -inf; every other tile runs
-// without any per-element test.
+// row maxima (with kDeferPV, the previous tile's deferred PV products go out
+// here); P^ of the first 64-key half and its PV products, which run on the
+// matrix cores while P^ of the second half is formed; then the second half's
+// PV products (with kDeferPV, kept for the next tile).  MASKED tiles (the
+// ragged last tile and the causal diagonal) set scores of invisible keys to
+// -inf; every other tile runs without any per-element test.
 template <int D, bool CAUSAL, int MODE, int RULE, bool MASKED>
 __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int kt, int N, const uint4 (&qop)[D / 64],
                                           int qsc, int q, uint4 ones, int one_sc, RowState& rs, v16f (&acc)[D / 32],
