@@ -240,3 +240,21 @@ def test_token_blocks_at_the_exponent_clamp_next_to_subnormal_blocks():
     _, _, vm = mx.rotate_quantize_qkv(x, x, x, rotate=False)
     torch.cuda.synchronize()
     assert torch.equal(ref.codes, vm.codes) and torch.equal(ref.scales, vm.scales)
+
+
+def test_qkv_launch_equals_three_calls_at_the_benchmark_shape():
+    """The benchmark's quantizer launch (one mxattn_rotate_quantize_qkv over the
+    full Wan-like Q, K, V) writes exactly what the three separate calls write;
+    the separate calls are compared with the oracle on sampled rows and blocks
+    by test_workload_quantizers_bit_exact."""
+    w = W.WORKLOADS[2]
+    say(f"qkv launch at the benchmark shape: {w.describe()}")
+    dev = {t: to_device(W.generate(w, t), w.dtype) for t in "qkv"}
+    refs = (mx.rotate_quantize(dev["q"], mx.AXIS_HEAD_DIM, rotate=True),
+            mx.rotate_quantize(dev["k"], mx.AXIS_HEAD_DIM, rotate=True),
+            mx.rotate_quantize(dev["v"], mx.AXIS_TOKEN, rotate=False))
+    outs = mx.rotate_quantize_qkv(dev["q"], dev["k"], dev["v"], rotate=True)
+    torch.cuda.synchronize()
+    for name, r, o in zip("qkv", refs, outs):
+        assert torch.equal(r.codes, o.codes), name
+        assert torch.equal(r.scales, o.scales), name
