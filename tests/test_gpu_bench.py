@@ -49,6 +49,13 @@ def test_bench_separate_quantizer_launches():
     assert q["rotate_quantize_k"]["us"] > 0 and q["quantize_v"]["us"] > 0
 
 
+@pytest.mark.gpu
+def test_bench_fused_q_step():
+    d = _run("--workload", "1", "--steps", "2", "--warmup", "1", "--no-cpu-baseline", "--fused-q")
+    assert d["config"]["fused_q"] is True and d["config"]["quantizer_launches"] == 2
+    assert d["forward"]["tflops"] > 0 and d["quantizer"]["quantize_v"]["us"] > 0
+
+
 def test_bench_refuses_more_than_one_gpu():
     """(CPU) the one-GPU scope is enforced before any GPU work."""
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
