@@ -129,19 +129,31 @@ __device__ __forceinline__ int kc_source_chunk(int G) {
 // 16-byte chunk that belongs in that (swizzled) granule.  The scale bytes are
 // few; they pass through registers and are scattered into their operand
 // order with small stores (scale_store).
-// LDS-destination copy of one 16-byte chunk per lane (device code only: the
-// builtin takes an LDS address-space pointer, which the host pass cannot form)
-__device__ __forceinline__ void dma16(const uint8_t* src, uint8_t* lds_base) {
+// Tile copies go through buffer descriptors: the tile's base address and
+// size live in scalar registers and each lane adds a 32-bit offset, so moving
+// to the next tile is scalar arithmetic only (with flat 64-bit addresses the
+// vector unit spent a 64-bit add per copy and tile).  An offset past `bytes`
+// reads zeros instead of faulting.  Device code only: the descriptor type and
+// the LDS address space do not exist in the host pass.
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(src, reinterpret_cast<__attribute__((address_space(3))) void*>(
-                                            reinterpret_cast<uintptr_t>(lds_base)),
-                                   16, 0, 0);
-#endif
+constexpr int kRawBufferWord3 = 0x00020000;  // descriptor word 3: raw dwords
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint8_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, bytes, kRawBufferWord3);
 }
+
+// LDS-destination copy of one 16-byte chunk per lane, from byte voff + soff
+// of the descriptor's range
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff, int soff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rsrc, reinterpret_cast<__attribute__((address_space(3))) void*>(reinterpret_cast<uintptr_t>(lds_base)), 16,
+      (int)voff, soff, 0, 0);
+}
+#endif
 
 // Per-lane source offsets of the DMA: loop-invariant, computed once.  The
 // wave index is uniform; keeping it scalar makes each LDS base (M0) a scalar
-// value, and 32-bit lane offsets let the loads use a scalar 64-bit base.
+// value.
 template <int D>
 struct DmaPlan {
   static constexpr int KU = kBc * D / 2 / 16 / 256;  // K^ granules per lane
@@ -164,10 +176,13 @@ __device__ __forceinline__ void codes_dma(const Params& p, const DmaPlan<D>& pla
   const uint32_t voff = (uint32_t)(plan.lds0 + 16 * (tid & 63));
   const uint8_t* kb = p.kc + (bh * p.Np + (int64_t)kt * kBc) * (D / 2);
   const uint8_t* vb = p.vc + (bh * NBp + (int64_t)kt * 4) * D * 16;
+#if defined(__HIP_DEVICE_COMPILE__)
+  const __amdgpu_buffer_rsrc_t kr = tile_rsrc(kb, kBc * D / 2), vr = tile_rsrc(vb, 64 * D);
 #pragma unroll
-  for (int u = 0; u < DmaPlan<D>::KU; ++u) dma16(kb + plan.koff[u], stage + L::KC + u * 4096 + plan.lds0);
+  for (int u = 0; u < DmaPlan<D>::KU; ++u) dma16(kr, plan.koff[u], 0, stage + L::KC + u * 4096 + plan.lds0);
 #pragma unroll
-  for (int u = 0; u < DmaPlan<D>::VU; ++u) dma16(vb + u * 4096 + voff, stage + L::VC + u * 4096 + plan.lds0);
+  for (int u = 0; u < DmaPlan<D>::VU; ++u) dma16(vr, voff, u * 4096, stage + L::VC + u * 4096 + plan.lds0);
+#endif
 }
 
 struct ScaleRegs {
@@ -181,12 +196,17 @@ template <int D>
 __device__ __forceinline__ ScaleRegs scale_load(const Params& p, int64_t bh, int kt, int tid) {
   const int NBp = p.Np / 32;
   ScaleRegs r = {0u, 0u};
+#if defined(__HIP_DEVICE_COMPILE__)
   if (tid < kBc) {
-    const uint8_t* ksrc = p.ks + (bh * p.Np + (int64_t)kt * kBc + tid) * (D / 32);
-    if constexpr (D == 128) r.ks = *reinterpret_cast<const uint32_t*>(ksrc);
-    else r.ks = *reinterpret_cast<const uint16_t*>(ksrc);
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(p.ks + (bh * p.Np + (int64_t)kt * kBc) * (D / 32), kBc * D / 32);
+    if constexpr (D == 128) r.ks = __builtin_amdgcn_raw_buffer_load_b32(kr, 4 * tid, 0, 0);
+    else r.ks = __builtin_amdgcn_raw_buffer_load_b16(kr, 2 * tid, 0, 0);
   }
-  if (tid < D) r.vs = *reinterpret_cast<const uint32_t*>(p.vs + (bh * NBp + (int64_t)kt * 4) * D + 4 * tid);
+  if (tid < D) {
+    const __amdgpu_buffer_rsrc_t vr = tile_rsrc(p.vs + (bh * NBp + (int64_t)kt * 4) * D, 4 * D);
+    r.vs = __builtin_amdgcn_raw_buffer_load_b32(vr, 4 * tid, 0, 0);
+  }
+#endif
   return r;
 }
 
@@ -575,8 +595,14 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
     for (int h = 0; h < NH; ++h)
       kop[t][h] = *reinterpret_cast<const uint4*>(buf + koff[h] + (D / 2) * (64 * (t >> 1) + 16 * (t & 1)));
   // the burst of score products runs at raised wave priority, so that it
-  // reaches the matrix core ahead of the co-resident wave's vector work
+  // reaches the matrix core ahead of the co-resident wave's vector work.  On
+  // unmasked tiles without deferred products, the first block maximum (which
+  // needs only the first two sub-tiles) is formed between the last products,
+  // so the wave's own vector work runs under its burst.
+  constexpr bool kDefer = kDeferPV<D, CAUSAL> && MODE != kModeStats && MODE != kModeDiag;
+  constexpr bool kSplit = !MASKED && !kDefer;
   v16f s[4];
+  float bmax[2];
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(1);
 #pragma unroll
@@ -586,16 +612,24 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
     for (int h = 0; h < NH; ++h)
       s[t] = mfma32_sel((t & 1) * NH + h, h, kop[t][h], qop[h], s[t], (t < 2) ? (int)ksw.x : (int)ksw.y, qsc);
   }
+  if constexpr (kSplit) {
+    bmax[0] = max32(s[0], s[1]);
+    // order: 2 NH + 1 products, then (4 vector instructions, 1 product) x (2 NH - 1)
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * NH + 1, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * NH - 1; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+  }
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_setprio(0);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- running max, block maxima, alpha (and the deferred PV products of
   // the previous tile, which must precede this tile's rescale)
-  constexpr bool kDefer = kDeferPV<D, CAUSAL> && MODE != kModeStats && MODE != kModeDiag;
   mask_scores<CAUSAL, MASKED>(s, kt, N, q, g);
-  float bmax[2];
-  bmax[0] = max32(s[0], s[1]);
+  if constexpr (!kSplit) bmax[0] = max32(s[0], s[1]);
   if constexpr (kDefer) issue_pending<D>(pend, acc, accl, ones, one_sc);
   bmax[1] = max32(s[2], s[3]);
   const float tmax = fmaxf(bmax[0], bmax[1]);
