@@ -32,6 +32,7 @@
 
 #include "internal.h"
 #include "mx_block.h"
+#include "quant_index.h"
 
 namespace mxattn_internal {
 namespace {
@@ -81,16 +82,12 @@ __device__ __forceinline__ void headdim_group(const QTensor& t, uint32_t qb, int
 #pragma unroll
   for (int it = 0; it < QU; ++it) {
     unit[it] = group * 256 * QU + it * 256 + threadIdx.x;
-    const int64_t row = unit[it] / BPR;
-    const int blk = (int)(unit[it] % BPR);
-    const int64_t bh = row / t.Np;
-    const int n = (int)(row % t.Np);
-    const bool live = unit[it] < t.total && n < t.N;
+    const HeaddimUnit w = headdim_unit(unit[it], t.Np, BPR);
+    const int64_t off = headdim_load_offset(w, t.total, unit[it], t.H, t.N, t.sB, t.sH, t.sN);
 #pragma unroll
     for (int k = 0; k < 4; ++k) raw[it][k] = make_uint4(0, 0, 0, 0);
-    if (live) {
-      const int64_t b = bh / t.H, h = bh % t.H;
-      const uint4* p = reinterpret_cast<const uint4*>(t.x + b * t.sB + h * t.sH + (int64_t)n * t.sN + 32 * blk);
+    if (off >= 0) {  // a padding row (n >= N) loads nothing
+      const uint4* p = reinterpret_cast<const uint4*>(t.x + off);
 #pragma unroll
       for (int k = 0; k < 4; ++k) raw[it][k] = p[k];
     }
@@ -128,16 +125,18 @@ __device__ __forceinline__ void tokens_group(const QTensor& t, uint32_t qb, int6
   const int NBp = t.Np / 32;
   const int64_t bh = gblk / NBp;
   const int kb = (int)(gblk % NBp);
-  const int64_t b = bh / t.H, h = bh % t.H;
   const int N = t.N;
   const int64_t sN = t.sN;
-  const uint16_t* base = t.x + b * t.sB + h * t.sH + (int64_t)(32 * kb) * sN + 2 * cp;
+  const uint16_t* lane_base = t.x + tokens_lane_base(bh, cp, t.H, t.sB, t.sH);
 
-  // all 32 loads are issued before any is used; only a block that crosses N
-  // (the last one) takes the guarded path, decided once per wave
+  // all 32 loads are issued before any is used; only a block that crosses or
+  // lies past N (the last one or few of a head) takes the guarded path,
+  // decided once per wave.  The guarded path reads each token clamped into
+  // [0, N) (a block wholly in the padding reads token N - 1) and discards the
+  // values past N, so no load leaves the tensor.
   uint32_t w[32];
-  if (__all(32 * kb + 31 < N)) {
-    const uint16_t* pt = base;
+  if (__all(tokens_block_inside(kb, N))) {
+    const uint16_t* pt = lane_base + (int64_t)(32 * kb) * sN;
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
       w[k] = *reinterpret_cast<const uint32_t*>(pt);
@@ -146,8 +145,8 @@ __device__ __forceinline__ void tokens_group(const QTensor& t, uint32_t qb, int6
   } else {
 #pragma unroll
     for (int k = 0; k < 32; ++k) {
-      const int tc = min(k, max(N - 1 - 32 * kb, 0));  // an in-range row to read from
-      const uint32_t wt = *reinterpret_cast<const uint32_t*>(base + (int64_t)tc * sN);
+      const uint32_t wt =
+          *reinterpret_cast<const uint32_t*>(lane_base + (int64_t)tokens_guarded_token(kb, k, N) * sN);
       w[k] = (32 * kb + k < N) ? wt : 0u;
     }
   }
