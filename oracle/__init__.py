@@ -47,6 +47,9 @@ def _load():
     lib.oracle_quantize_block.restype = ctypes.c_int
     lib.oracle_quantize_block.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_double, u8p, ctypes.c_void_p]
+    lib.oracle_p_block_allowance.restype = ctypes.c_int
+    lib.oracle_p_block_allowance.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                             ctypes.c_double, ctypes.c_void_p, ctypes.c_void_p]
     lib.oracle_decode_half.restype = ctypes.c_float
     lib.oracle_decode_half.argtypes = [ctypes.c_uint16, ctypes.c_int]
     lib.oracle_hadamard_rotate_f32.restype = None
@@ -132,6 +135,17 @@ def quantize_block(x, rule: int = RULE_UOS, q: float = 0.0):
     sb = ctypes.c_uint8(0)
     e = _load().oracle_quantize_block(_ptr(x), x.size, rule, float(q), ctypes.byref(sb), _ptr(codes))
     return sb.value, codes, e
+
+
+def p_block_allowance(p, rule: int = RULE_UOS, q: float = 0.0, delta: float = 0.0, exact_ref: float = 0.0):
+    """One 32-key block of the softmax-path quantizer with its decision
+    allowance.  Returns (dequantized P^ [32], allowance dp [32], exponent)."""
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    assert p.shape == (32,)
+    ph = np.empty(32, np.float64)
+    dp = np.empty(32, np.float64)
+    e = _load().oracle_p_block_allowance(_ptr(p), rule, float(q), float(delta), float(exact_ref), _ptr(ph), _ptr(dp))
+    return ph, dp, e
 
 
 def decode_half(bits: int, dtype: int) -> float:

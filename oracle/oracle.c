@@ -461,18 +461,30 @@ static void load_query(const attn_ctx* c, int64_t b, int64_t h, int i, double* q
 }
 
 /* Quantize one 32-key block of exponentials p[0..31] (a tile segment, zeros
- * for keys that are masked or past N) and return the dequantized values in
- * ph.  If delta > 0, also write into dp the largest change of each element
- * that a decision within relative margin delta of its boundary could make:
- * an element lying near a rounding midpoint may round to the neighbouring
- * grid point, and a block maximum lying near a scale boundary may select the
- * neighbouring exponent (the whole block is then re-projected). */
-static int quantize_p_block(const oracle_attn_cfg* g, const double* p, double* ph, double* dp) {
+ * for keys that are masked or past N) [P1 Alg. 1 applied to P~, Eq. 44] and
+ * return the dequantized values in ph.  If dp is given, also write into it
+ * the largest change of each element that a decision lying within relative
+ * margin delta of its threshold could make (the decision allowance):
+ *   - an element whose normalized value p/2^e lies within delta of a
+ *     rounding midpoint may round to the neighbouring grid point;
+ *   - a block whose normalized maximum lies within delta of one end of the
+ *     rule's range (lo, hi] may take the neighbouring exponent, and every
+ *     element of the block is then re-projected.
+ * The margin stands for the rounding of a binary32 evaluation of P~.  One
+ * value is not subject to it: the exponential at the row maximum is
+ * exp(0) = 1 exactly, and in the post-normalization mode P = 1/l* at the row
+ * maximum lies below 1 exactly when l* > 1 (gamma P below gamma, for a
+ * power-of-two gamma).  With exact_ref > 0, the block's maximum is that
+ * element, known exactly relative to exact_ref (1 or gamma), so a scale
+ * boundary equal to exact_ref (lo 2^e or hi 2^e, as OCP has at powers of two)
+ * is not a close decision and offers no alternative.  Returns the block
+ * exponent. */
+int oracle_p_block_allowance(const double* p, int rule, double q, double delta, double exact_ref, double* ph,
+                             double* dp) {
   uint8_t codes[32], sb;
-  int e = oracle_quantize_block(p, 32, g->rule, g->q, &sb, codes);
+  int e = oracle_quantize_block(p, 32, rule, q, &sb, codes);
   for (int t = 0; t < 32; ++t) ph[t] = dequant(codes[t], sb);
   if (!dp) return e;
-  const double delta = g->amb_delta;
   for (int t = 0; t < 32; ++t) {
     dp[t] = 0.0;
     double y = ldexp(p[t], -e);
@@ -490,15 +502,14 @@ static int quantize_p_block(const oracle_attn_cfg* g, const double* p, double* p
   if (M <= 0.0) return e;
   /* normalized block max and the two ends of its admissible interval */
   double r = ldexp(M, -e), hi, lo;
-  switch (g->rule) {
+  switch (rule) {
     case ORACLE_RULE_UOS: hi = 7.25; lo = 3.625; break;
-    case ORACLE_RULE_CEIL_Q: hi = g->q; lo = 0.5 * g->q; break;
     case ORACLE_RULE_OCP: hi = 8.0; lo = 4.0; break;
-    default: hi = g->q; lo = 0.5 * g->q; break;
+    default: hi = q; lo = 0.5 * q; break; /* ceiling rule: M/2^e in (q/2, q] */
   }
   int alts[2], na = 0;
-  if (fabs(r - hi) <= delta * hi && e < 127) alts[na++] = e + 1;
-  if (fabs(r - lo) <= delta * lo && e > -127) alts[na++] = e - 1;
+  if (fabs(r - hi) <= delta * hi && e < 127 && !(ldexp(hi, e) == exact_ref)) alts[na++] = e + 1;
+  if (fabs(r - lo) <= delta * lo && e > -127 && !(ldexp(lo, e) == exact_ref)) alts[na++] = e - 1;
   for (int a = 0; a < na; ++a) {
     int ea = alts[a];
     for (int t = 0; t < 32; ++t) {
@@ -509,6 +520,23 @@ static int quantize_p_block(const oracle_attn_cfg* g, const double* p, double* p
   }
   return e;
 }
+
+static int quantize_p_block(const oracle_attn_cfg* g, const double* p, double exact_ref, double* ph, double* dp) {
+  return oracle_p_block_allowance(p, g->rule, g->q, g->amb_delta, exact_ref, ph, dp);
+}
+
+/* Whether the row maximum s1 stands alone: the runner-up s2 (-inf if none)
+ * gives exp(s2 - s1) < 1 - delta, so a binary32 evaluation of the scores
+ * cannot make another key the maximum.  An exact tie of two keys is not
+ * alone either. */
+static int max_stands_alone(double s1, double s2, double delta) {
+  return s2 == -INFINITY || exp(s2 - s1) < 1.0 - delta;
+}
+
+/* Smallest mass rho = l* - 1 of the keys other than the row maximum that a
+ * binary32 sum of binary32 exponentials still sees as nonzero: with at most
+ * 2^17 keys, rho >= 2^-100 has a term >= 2^-117, a normal binary32. */
+#define ORACLE_RHO_VISIBLE 0x1p-100
 
 static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
   const attn_ctx* c = (const attn_ctx*)vctx;
@@ -567,14 +595,25 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
       /* Materialized-P diagnostic [P1 Sec. 5.5.2]: exact softmax first, then
        * quantize the normalized probabilities in aligned 32-key blocks and
        * accumulate O = Q(P) V^ with no renormalization. */
-      double ms = -INFINITY, ls = 0.0;
-      for (int j = 0; j < jvis; ++j) if (sc[j] > ms) ms = sc[j];
+      double ms = -INFINITY, s2 = -INFINITY, ls = 0.0, rho = 0.0;
+      int jmax = 0;
+      for (int j = 0; j < jvis; ++j) {
+        if (sc[j] > ms) { s2 = ms; ms = sc[j]; jmax = j; }
+        else if (sc[j] > s2) s2 = sc[j];
+      }
       for (int j = 0; j < jvis; ++j) ls += exp(sc[j] - ms);
+      /* rho = l* - 1, summed without the maximum's exp(0) = 1 so that a tiny
+       * rho keeps its relative precision */
+      for (int j = 0; j < jvis; ++j) if (j != jmax) rho += exp(sc[j] - ms);
+      /* P at the row maximum, 1/l*, is below 1 exactly when rho > 0: an
+       * exact decision while rho stays visible in binary32 and no other key
+       * ties the maximum */
+      const int exact_max = max_stands_alone(ms, s2, g->amb_delta) && rho >= ORACLE_RHO_VISIBLE && rho < 1.0;
       double sum_hat = 0.0;
       for (int j0 = 0; j0 < jvis; j0 += 32) {
         double pb[32], hb[32], db[32];
         for (int t = 0; t < 32; ++t) pb[t] = (j0 + t < jvis) ? exp(sc[j0 + t] - ms) / ls : 0.0;
-        quantize_p_block(g, pb, hb, want_amb ? db : NULL);
+        quantize_p_block(g, pb, (exact_max && jmax >= j0 && jmax < j0 + 32) ? 1.0 : 0.0, hb, want_amb ? db : NULL);
         for (int t = 0; t < 32 && j0 + t < jvis; ++t) {
           sum_hat += hb[t];
           for (int ch = 0; ch < d; ++ch) o[ch] += hb[t] * V[(int64_t)(j0 + t) * d + ch];
@@ -595,6 +634,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
     /* Online softmax over key tiles in ascending order [P1 Alg. 2;
      * Eqs. 3-7 with Eqs. 44-48 (PNQ) or Eq. 42 (direct)]. */
     double m = -INFINITY, l = 0.0, al = 0.0;
+    double s2 = -INFINITY; /* runner-up of the scores seen so far */
     int ntiles_seen = 0;
     for (int tile = 0; tile < T; ++tile) {
       const int j0 = tile * Bc;
@@ -605,13 +645,25 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
       double smax = -INFINITY;
       for (int j = j0; j < j1; ++j) if (sc[j] > smax) smax = sc[j];
       const double m_new = m > smax ? m : smax;                 /* Eq. 3  */
+      {
+        /* runner-up over every key seen so far (tiles 0..tile) */
+        double s1 = m;
+        for (int j = j0; j < j1; ++j) {
+          if (sc[j] > s1) { s2 = s1; s1 = sc[j]; }
+          else if (sc[j] > s2) s2 = sc[j];
+        }
+      }
+      /* keys at the running maximum have P~ = exp(0) = 1 exactly */
+      const int alone = max_stands_alone(m_new, s2, g->amb_delta);
       const double alpha = (m == -INFINITY) ? 0.0 : exp(m - m_new); /* Eq. 4 */
       double* P = pt + j0;
       double* Ph = ph + j0;
       double* D = dp + j0;
       for (int t = 0; t < Bc; ++t) P[t] = (j0 + t < j1) ? exp(sc[j0 + t] - m_new) : 0.0; /* Eq. 5 */
       for (int t0 = 0; t0 < Bc; t0 += 32) {
-        if (quantize_p) quantize_p_block(g, P + t0, Ph + t0, want_amb ? D + t0 : NULL); /* Eq. 44 */
+        int one = 0; /* the block holds the running maximum */
+        for (int t = t0; t < t0 + 32; ++t) one |= (j0 + t < j1 && sc[j0 + t] == m_new);
+        if (quantize_p) quantize_p_block(g, P + t0, (alone && one) ? 1.0 : 0.0, Ph + t0, want_amb ? D + t0 : NULL); /* Eq. 44 */
         else for (int t = 0; t < 32; ++t) Ph[t0 + t] = P[t0 + t];
       }
       double sum_hat = 0.0, sum_til = 0.0;
@@ -767,14 +819,25 @@ static void diag_item(void* vctx, int64_t item, void* scratch_raw) {
     const int i = c->rows ? c->rows[r] : r;
     load_query(&ac, b, h, i, qv, buf, codes, blk);
     const int jvis = g->causal ? (i + 1 < N ? i + 1 : N) : N;
-    double ms = -INFINITY, ls = 0.0;
+    double ms = -INFINITY, s2 = -INFINITY, ls = 0.0, rho = 0.0;
+    int jmax = 0;
     for (int j = 0; j < jvis; ++j) {
       double acc = 0.0;
       for (int t = 0; t < d; ++t) acc += qv[t] * K[(int64_t)j * d + t];
       sc[j] = acc * inv_sqrt_d;
-      if (sc[j] > ms) ms = sc[j];
+      if (sc[j] > ms) { s2 = ms; ms = sc[j]; jmax = j; }
+      else if (sc[j] > s2) s2 = sc[j];
     }
     for (int j = 0; j < jvis; ++j) ls += exp(sc[j] - ms);
+    for (int j = 0; j < jvis; ++j) if (j != jmax) rho += exp(sc[j] - ms);
+    /* gamma P at the row maximum is gamma / l*, below gamma exactly when
+     * rho = l* - 1 > 0; for a power-of-two gamma that is an exact decision
+     * while rho stays visible in binary32 and no other key ties the maximum
+     * (see oracle_p_block_allowance) */
+    int gexp;
+    const int gamma_pow2 = frexp(c->gamma, &gexp) == 0.5;
+    const int exact_max = gamma_pow2 && max_stands_alone(ms, s2, g->amb_delta) && rho >= ORACLE_RHO_VISIBLE &&
+                          rho < 1.0;
     double out[6] = {0, 0, 0, 0, 0, 0}, amb = 0.0;
     for (int j0 = 0; j0 < jvis; j0 += 32) {
       double P[32], gp[32], hb[32], db[32];
@@ -782,7 +845,8 @@ static void diag_item(void* vctx, int64_t item, void* scratch_raw) {
         P[t] = (j0 + t < jvis) ? exp(sc[j0 + t] - ms) / ls : 0.0;
         gp[t] = c->gamma * P[t];
       }
-      const int e = quantize_p_block(g, gp, hb, c->amb ? db : NULL);
+      const int e = quantize_p_block(g, gp, (exact_max && jmax >= j0 && jmax < j0 + 32) ? c->gamma : 0.0, hb,
+                                     c->amb ? db : NULL);
       for (int t = 0; t < 32 && j0 + t < jvis; ++t) {
         const double ph = hb[t] / c->gamma, diff = ph - P[t];
         out[0] += ph;

@@ -77,6 +77,19 @@ void oracle_scale_exponents(const double* M, int64_t n, int rule, double q, int3
 int oracle_quantize_block(const double* x, int n, int rule, double q,
                           uint8_t* scale_byte, uint8_t* codes);
 
+/* One 32-key block of the softmax-path quantizer [P1 Alg. 1 on P~, Eq. 44]
+ * with its decision allowance: ph[t] = the dequantized P^, and (dp non-NULL)
+ * dp[t] = the largest change of P^_t that a decision within relative margin
+ * delta of its threshold could make -- an element near a rounding midpoint,
+ * or a block maximum near an end of the rule's range (then every element is
+ * re-projected at the neighbouring exponent).  exact_ref > 0 says the block's
+ * maximum is the row maximum's element, known exactly relative to exact_ref
+ * (P~ = exp(0) = 1 online; gamma / l* < gamma after normalization): a scale
+ * boundary equal to exact_ref then offers no alternative.  Returns the
+ * clamped block exponent. */
+int oracle_p_block_allowance(const double* p, int rule, double q, double delta, double exact_ref, double* ph,
+                             double* dp);
+
 /* Exact decode of a 16-bit element to binary32. */
 float oracle_decode_half(uint16_t bits, int dtype);
 

@@ -191,6 +191,17 @@ static void check_scalars(void) {
   for (int i = 0; i < 128; ++i) r[i] = (float)(next_unit() - 0.5);
   oracle_hadamard_rotate_f32(r, 64);
   oracle_hadamard_rotate_f32(r, 128);
+  /* the block allowance over both rules, zero / tiny / boundary blocks and
+   * both exact references */
+  double p[32], ph[32], dp[32];
+  for (int rule = 0; rule < 4; ++rule)
+    for (int kind = 0; kind < 4; ++kind) {
+      for (int i = 0; i < 32; ++i) p[i] = kind == 0 ? 0.0 : (kind == 1 ? 0x1p-140 * next_unit() : next_unit());
+      if (kind == 3) p[7] = 1.0;
+      sink += oracle_p_block_allowance(p, rule, 6.5, 1e-3, kind == 3 ? 1.0 : 0.0, ph, dp) * 0.0;
+      sink += oracle_p_block_allowance(p, rule, 6.5, 0.0, 0.0, ph, NULL) * 0.0;
+      for (int i = 0; i < 32; ++i) sink += ph[i] * 0.0 + dp[i] * 0.0;
+    }
   (void)sink;
 }
 

@@ -633,6 +633,276 @@ def test_decision_allowance_is_nonnegative_and_off_by_default():
     assert (r1["out"] == r0["out"]).all()
 
 
+# ---- the decision allowance (binary32 evaluations of P~ against the
+# binary64 oracle; the margin delta stands for their rounding)
+
+MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)  # E2M1 decision boundaries [P1 Eq. 68]
+RANGE = {oracle.RULE_UOS: (3.625, 7.25), oracle.RULE_OCP: (4.0, 8.0)}  # normalized block max (lo, hi]
+
+
+def _far_from_every_threshold(p, rule, e, delta):
+    """True when every normalized element p/2^e lies farther than delta
+    (relative) from every rounding midpoint and the normalized block maximum
+    farther than delta from both ends of the rule's range -- computed here
+    from the printed grid and the range of the rule."""
+    y = np.ldexp(p, -e)
+    for mid in MIDPOINTS:
+        if (np.abs(y - mid) <= delta * mid).any():
+            return False
+    lo, hi = RANGE[rule]
+    r = y.max()
+    return r > 0 and abs(r - lo) > delta * lo and abs(r - hi) > delta * hi
+
+
+@pytest.mark.parametrize("rule", [oracle.RULE_UOS, oracle.RULE_OCP])
+def test_allowance_is_zero_far_from_every_threshold(rule):
+    """A block whose every decision lies farther than delta from its
+    threshold has no allowance; one whose decision lies within delta/2 of its
+    threshold has an allowance of at least the step that decision can take."""
+    rng = np.random.default_rng(5)
+    delta = 2.0 ** -8
+    far = near = 0
+    for _ in range(3000):
+        p = np.exp(rng.normal(0.0, 2.0, 32)) * 2.0 ** rng.integers(-20, 20)
+        ph, dp, e = oracle.p_block_allowance(p, rule, delta=delta)
+        if _far_from_every_threshold(p, rule, e, delta):
+            far += 1
+            assert (dp == 0).all()
+        # plant one element within delta/2 of a midpoint at this exponent
+        t = int(rng.integers(0, 32))
+        c = int(rng.integers(0, 7))
+        q = p.copy()
+        q[t] = np.ldexp(MIDPOINTS[c] * (1 + rng.uniform(-0.5, 0.5) * delta), e)
+        if q.max() != p.max() or q[t] >= p.max():
+            continue
+        _, dq, eq = oracle.p_block_allowance(q, rule, delta=delta)
+        if eq == e:
+            near += 1
+            grid = (0, 0.5, 1, 1.5, 2, 3, 4, 6)
+            assert dq[t] >= np.ldexp(grid[c + 1] - grid[c], e)
+    assert far > 100 and near > 1000
+
+
+def test_allowance_closed_form_blocks():
+    """Hand-computed blocks.  UOS [P1 Alg. 1]: max 6 gives e = 0; an element at
+    the midpoint 2.5 may round to 2 or 3 (allowance 1).  A max at exactly the
+    boundary 7.25 (e = 0, saturating to 6) may take e = 1, where it rounds to
+    8: allowance 2.  Moving it up by 2 delta gives e = 1 with 3.625 (1 + 2
+    delta), clear of the boundary; by delta/2, still within it."""
+    delta = 2.0 ** -13
+    p = np.zeros(32)
+    p[0], p[5] = 6.0, 2.5
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_UOS, delta=delta)
+    assert e == 0 and ph[0] == 6 and ph[5] == 2 and dp[5] == 1 and (np.delete(dp, 5) == 0).all()
+    p = np.zeros(32)
+    p[3] = 7.25
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_UOS, delta=delta)
+    assert e == 0 and ph[3] == 6 and dp[3] == 2 and (np.delete(dp, 3) == 0).all()
+    p[3] = 7.25 * (1 + 2 * delta)
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_UOS, delta=delta)
+    assert e == 1 and (dp == 0).all()
+    p[3] = 7.25 * (1 + delta / 2)
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_UOS, delta=delta)
+    assert e == 1 and dp[3] > 0
+
+
+def test_allowance_exempts_exact_one_only():
+    """OCP puts 1 on a scale boundary (floor(log2 1) - 2 = -2, normalized max
+    4 = lo).  P~ = exp(0) = 1 at the row maximum is exact on any hardware, so
+    with exact_ref = 1 that boundary offers no alternative; without it the
+    alternative e = -3 (1 saturates to 6/8) is allowed.  The same holds for
+    P = 1/l* < 1 next to the boundary from below.  Other boundaries are not
+    exempt."""
+    delta = 2.0 ** -13
+    p = np.zeros(32)
+    p[7], p[9] = 1.0, 0.01
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_OCP, delta=delta)
+    assert e == -2 and ph[7] == 1 and dp[7] == 0.25
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_OCP, delta=delta, exact_ref=1.0)
+    assert e == -2 and (dp == 0).all()
+    p[7] = 1.0 / (1.0 + 1e-9)  # post-normalization P at the row maximum
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_OCP, delta=delta)
+    assert e == -3 and ph[7] == 0.75 and dp[7] == 0.25
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_OCP, delta=delta, exact_ref=1.0)
+    assert e == -3 and (dp == 0).all()
+    p[7] = 0.5 * (1 + delta / 4)  # next to the boundary 1/2: not exempt
+    ph, dp, e = oracle.p_block_allowance(p, oracle.RULE_OCP, delta=delta, exact_ref=1.0)
+    assert e == -3 and dp[7] > 0
+
+
+def _one_hot_inputs(N, d, gap, tie=False, seed=0):
+    """Q = 1 on channel 0 plus small noise elsewhere; K noise on the other
+    channels, 0 on channel 0, except key 5 (in the first tile) with a large
+    channel-0 entry: its score exceeds the rest by about `gap`.  `tie` gives
+    key 45 the same channel-0 entry, an exact tie of the maximum."""
+    rng = np.random.default_rng(seed)
+    q = 0.3 * rng.standard_normal((1, 1, N, d))
+    q[..., 0] = 1.0
+    k = 0.3 * rng.standard_normal((1, 1, N, d))
+    k[..., 0] = 0.0
+    j0 = 5
+    k[0, 0, j0, 0] = gap * math.sqrt(d)
+    if tie:
+        k[0, 0, j0 + 40] = k[0, 0, j0]
+    v = rng.standard_normal((1, 1, N, d))
+    return (W.to_bits(q, W.BF16), W.to_bits(k, W.BF16), W.to_bits(v, W.BF16))
+
+
+@pytest.mark.parametrize("p_mode", [oracle.P_DIRECT, oracle.P_PNQ])
+def test_one_hot_row_has_no_allowance_under_ocp(p_mode):
+    """A row with one dominant key: P~ = 1 there, every other P~ below
+    e^-20, far under the first midpoint at any exponent the block can take.
+    Under OCP (unrotated, the vanilla baseline) nothing is a close decision:
+    amb = 0.  A second key tying the maximum makes the row's maximum
+    uncertain (binary32 scores may break the tie either way), and the
+    allowance appears."""
+    N, d, delta = 96, 32, 2.0 ** -13
+    q, k, v = _one_hot_inputs(N, d, gap=24.0)
+    r = oracle.attention(q, k, v, W.BF16, 1, 1, N, d, rotate=False, rule=oracle.RULE_OCP, p_mode=p_mode,
+                         kv_tile=32, amb_delta=delta)
+    assert (r["amb"] == 0).all()
+    q, k, v = _one_hot_inputs(N, d, gap=24.0, tie=True)
+    r = oracle.attention(q, k, v, W.BF16, 1, 1, N, d, rotate=False, rule=oracle.RULE_OCP, p_mode=p_mode,
+                         kv_tile=32, amb_delta=delta)
+    assert r["amb"].max() > 0
+
+
+def test_postnorm_one_hot_row_allowance_follows_rho():
+    """Post-normalization under OCP: at the row maximum P = 1/l* with
+    l* = 1 + rho.  For rho > 0 it lies just below 1, so e = -3 and it
+    saturates to 6/8 = 0.75 [P1 Sec. 5.5.2, Eq. 10].  While rho is large
+    enough for binary32 to see (gap 24: rho ~ e^-22 N after K's OCP
+    quantization), that is an exact decision: amb = 0.  With rho below
+    2^-100 (gap 200: rho ~ e^-181 N) the decision is left open."""
+    N, d, delta = 96, 32, 2.0 ** -13
+    for gap, open_ in ((24.0, False), (200.0, True)):
+        q, k, v = _one_hot_inputs(N, d, gap=gap)
+        r = oracle.attention(q, k, v, W.BF16, 1, 1, N, d, rotate=False, rule=oracle.RULE_OCP,
+                             p_mode=oracle.P_POSTNORM, kv_tile=32, amb_delta=delta)
+        assert abs(r["rowsum"][0, 0].max() - 0.75) < 1e-6 or open_
+        assert (r["amb"].max() > 0) == open_
+
+
+def _forced_attention(qh, kh, vh, Bc, causal, rule, p_mode, delta, force, rows):
+    """Alg. 2 (PNQ / DIRECT) or the post-normalization mode re-stated over
+    dequantized q^, k^, v^ for the listed rows, with one hook:
+    force(i, j0, p, ph, exact_ref) returns the quantized block used for row i,
+    keys j0..j0+31 (ph is the plain block quantization of p).  exact_ref is 1
+    for a block holding the row maximum's element when that maximum stands
+    alone (runner-up below (1 - delta) of it; for post-normalization also
+    2^-100 <= l* - 1 < 1), else 0."""
+    Nq, d = qh.shape
+    N = kh.shape[0]
+    S = qh @ kh.T / math.sqrt(d)
+    out = {}
+    for i in rows:
+        vis = np.arange(N) <= i if causal else np.ones(N, bool)
+        if p_mode == oracle.P_POSTNORM:
+            s = np.where(vis, S[i], -np.inf)
+            jm = int(np.argmax(s))
+            srt = np.sort(s[vis])
+            e = np.exp(s - s[jm])
+            rho = e.sum() - 1.0 if e.sum() - 1.0 > 1e-3 else np.delete(e, jm).sum()
+            alone = len(srt) < 2 or math.exp(srt[-2] - srt[-1]) < 1 - delta
+            exact = alone and 2.0 ** -100 <= rho < 1
+            P = e / e.sum()
+            o = np.zeros(d)
+            for b0 in range(0, N, 32):
+                pb = np.zeros(32)
+                pb[:min(32, N - b0)] = P[b0:b0 + 32]
+                ref = 1.0 if exact and b0 <= jm < b0 + 32 else 0.0
+                ph = force(i, b0, pb, oracle.p_block_allowance(pb, rule)[0], ref)
+                o += ph[:min(32, N - b0)] @ vh[b0:b0 + 32]
+            out[i] = o
+            continue
+        m, l, o = -np.inf, 0.0, np.zeros(d)
+        seen = []
+        for j0 in range(0, N, Bc):
+            idx = [j for j in range(j0, min(j0 + Bc, N)) if vis[j]]
+            if not idx:
+                continue
+            seen.extend(S[i, idx])
+            srt = np.sort(seen)
+            mn = max(m, S[i, idx].max())
+            alone = len(srt) < 2 or math.exp(srt[-2] - srt[-1]) < 1 - delta
+            a = 0.0 if m == -np.inf else math.exp(m - mn)
+            pt = np.zeros(Bc)
+            pt[np.array(idx) - j0] = np.exp(S[i, idx] - mn)
+            ph = np.zeros(Bc)
+            for b0 in range(0, Bc, 32):
+                pb = pt[b0:b0 + 32]
+                ref = 1.0 if alone and (pb == 1.0).any() else 0.0
+                ph[b0:b0 + 32] = force(i, j0 + b0, pb, oracle.p_block_allowance(pb, rule)[0], ref)
+            l = a * l + (pt.sum() if p_mode == oracle.P_DIRECT else ph.sum())
+            o = a * o + ph[np.array(idx) - j0] @ vh[idx]
+            m = mn
+        out[i] = o / l
+    return out
+
+
+def _alternatives(p, ph, dp, rule):
+    """Every single decision of a block flipped: an element with dp > 0 moved
+    to its other grid neighbour, or the whole block re-projected at e +- 1
+    when that stays within dp (a flagged scale alternative)."""
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    alts = []
+    e = oracle.p_block_allowance(p, rule)[2]
+    for t in np.nonzero(dp > 0)[0]:
+        y = math.ldexp(p[t], -e)
+        below = grid[grid <= y].max()
+        above = grid[grid >= y].min() if y <= 6 else 6.0
+        for g in (below, above):
+            val = math.ldexp(g, e)
+            if val != ph[t] and abs(val - ph[t]) <= dp[t]:
+                a = ph.copy()
+                a[t] = val
+                alts.append(a)
+    for ea in (e - 1, e + 1):
+        a = np.array([math.ldexp(grid[oracle.e2m1_project(math.ldexp(x, -ea))], ea) for x in p])
+        if (a != ph).any() and (np.abs(a - ph) <= dp).all():
+            alts.append(a)
+    return alts
+
+
+@pytest.mark.parametrize("p_mode", [oracle.P_PNQ, oracle.P_DIRECT, oracle.P_POSTNORM])
+@pytest.mark.parametrize("rule", [oracle.RULE_UOS, oracle.RULE_OCP])
+def test_allowance_bounds_every_flagged_decision_forced(p_mode, rule):
+    """amb bounds how far O_i moves when decisions within the margin go the
+    other way.  With a wide margin (many flagged decisions), each flagged
+    decision is forced the other way, one at a time, in an independent
+    re-statement of the forward: the output row moves by at most amb, channel
+    by channel.  The re-statement without forcing equals the oracle."""
+    N, d, Bc, delta = 80, 32, 32, 0.05
+    x = W.custom(1, 1, N, d, seed=50 + rule + 3 * p_mode, scale=2.0)
+    qh, kh, vh = quantized_head(x["q"], x["k"], x["v"], W.BF16, N, d, rotate=False, rule=rule)
+    r = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, causal=True, rotate=False, rule=rule,
+                         p_mode=p_mode, kv_tile=Bc, amb_delta=delta)
+    rows = list(range(N))
+    base = _forced_attention(qh, kh, vh, Bc, True, rule, p_mode, delta, lambda i, j0, p, ph, ref: ph, rows)
+    for i in rows:
+        assert np.allclose(base[i], r["out"][0, 0, i], rtol=1e-12, atol=1e-12)
+    amb = r["amb"][0, 0]
+    flips = 0
+    for i in rows:
+        blocks = []
+
+        def record(ii, j0, p, ph, ref):
+            blocks.append((j0, p.copy(), ph.copy(), ref))
+            return ph
+
+        _forced_attention(qh, kh, vh, Bc, True, rule, p_mode, delta, record, [i])
+        for j0, p, ph, ref in blocks:
+            _, dp, _ = oracle.p_block_allowance(p, rule, delta=delta, exact_ref=ref)
+            for alt in _alternatives(p, ph, dp, rule):
+                def swap(ii, jj, pp, hh, rr, alt=alt, j0=j0):
+                    return alt if jj == j0 else hh
+                forced = _forced_attention(qh, kh, vh, Bc, True, rule, p_mode, delta, swap, [i])[i]
+                moved = np.abs(forced - base[i])
+                assert (moved <= amb[i] * (1 + 1e-9) + 1e-15).all(), (i, j0)
+                flips += 1
+    assert flips > 20
+
+
 def test_absmass_equals_output_for_nonnegative_values():
     """absmass is the output with |V^| in place of V^: for V >= 0 they coincide."""
     N, d = 150, 64
