@@ -609,10 +609,16 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
        * exact decision while rho stays visible in binary32 and no other key
        * ties the maximum */
       const int exact_max = max_stands_alone(ms, s2, g->amb_delta) && rho >= ORACLE_RHO_VISIBLE && rho < 1.0;
+      /* P at the row maximum is 1/l* = 1/(1 + rho), strictly below 1 when
+       * rho > 0; for rho < 2^-53 binary64 rounds it up to 1, onto OCP's
+       * scale boundary.  The largest binary64 below 1 stands in for it: no
+       * threshold of the block quantizer lies between the two. */
+      const double pmax = (rho > 0.0 && 1.0 / ls == 1.0) ? nextafter(1.0, 0.0) : 1.0 / ls;
       double sum_hat = 0.0;
       for (int j0 = 0; j0 < jvis; j0 += 32) {
         double pb[32], hb[32], db[32];
-        for (int t = 0; t < 32; ++t) pb[t] = (j0 + t < jvis) ? exp(sc[j0 + t] - ms) / ls : 0.0;
+        for (int t = 0; t < 32; ++t)
+          pb[t] = (j0 + t >= jvis) ? 0.0 : (j0 + t == jmax ? pmax : exp(sc[j0 + t] - ms) / ls);
         quantize_p_block(g, pb, (exact_max && jmax >= j0 && jmax < j0 + 32) ? 1.0 : 0.0, hb, want_amb ? db : NULL);
         for (int t = 0; t < 32 && j0 + t < jvis; ++t) {
           sum_hat += hb[t];
@@ -838,11 +844,14 @@ static void diag_item(void* vctx, int64_t item, void* scratch_raw) {
     const int gamma_pow2 = frexp(c->gamma, &gexp) == 0.5;
     const int exact_max = gamma_pow2 && max_stands_alone(ms, s2, g->amb_delta) && rho >= ORACLE_RHO_VISIBLE &&
                           rho < 1.0;
+    /* P at the row maximum: 1/(1 + rho), kept below 1 when rho > 0 (see the
+     * post-normalization mode of the attention forward) */
+    const double pmax = (rho > 0.0 && 1.0 / ls == 1.0) ? nextafter(1.0, 0.0) : 1.0 / ls;
     double out[6] = {0, 0, 0, 0, 0, 0}, amb = 0.0;
     for (int j0 = 0; j0 < jvis; j0 += 32) {
       double P[32], gp[32], hb[32], db[32];
       for (int t = 0; t < 32; ++t) {
-        P[t] = (j0 + t < jvis) ? exp(sc[j0 + t] - ms) / ls : 0.0;
+        P[t] = (j0 + t >= jvis) ? 0.0 : (j0 + t == jmax ? pmax : exp(sc[j0 + t] - ms) / ls);
         gp[t] = c->gamma * P[t];
       }
       const int e = quantize_p_block(g, gp, (exact_max && jmax >= j0 && jmax < j0 + 32) ? c->gamma : 0.0, hb,

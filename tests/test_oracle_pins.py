@@ -772,10 +772,12 @@ def test_postnorm_one_hot_row_allowance_follows_rho():
     l* = 1 + rho.  For rho > 0 it lies just below 1, so e = -3 and it
     saturates to 6/8 = 0.75 [P1 Sec. 5.5.2, Eq. 10].  While rho is large
     enough for binary32 to see (gap 24: rho ~ e^-22 N after K's OCP
-    quantization), that is an exact decision: amb = 0.  With rho below
-    2^-100 (gap 200: rho ~ e^-181 N) the decision is left open."""
+    quantization; gap 60: rho ~ e^-68 N ~ 2^-91, below binary64's 2^-53
+    next to 1, so 1/l* must not round up to the boundary 1), that is an
+    exact decision: amb = 0.  With rho below 2^-100 (gap 200: rho ~ e^-181 N)
+    the decision is left open."""
     N, d, delta = 96, 32, 2.0 ** -13
-    for gap, open_ in ((24.0, False), (200.0, True)):
+    for gap, open_ in ((24.0, False), (60.0, False), (200.0, True)):
         q, k, v = _one_hot_inputs(N, d, gap=gap)
         r = oracle.attention(q, k, v, W.BF16, 1, 1, N, d, rotate=False, rule=oracle.RULE_OCP,
                              p_mode=oracle.P_POSTNORM, kv_tile=32, amb_delta=delta)
