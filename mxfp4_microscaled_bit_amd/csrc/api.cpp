@@ -327,7 +327,7 @@ size_t mxattn_reference_modes_workspace_bytes(mxattn_shape shape, int32_t p_mode
   if (p_mode != MXATTN_P_PNQ && p_mode != MXATTN_P_DIRECT && p_mode != MXATTN_P_POSTNORM) return 0;
   size_t total = 3 * (round256(codes_bytes(shape, 0)) + round256(scales_bytes(shape, 0)));
   if (p_mode == MXATTN_P_POSTNORM)
-    total += round256((size_t)shape.B * shape.H * padded_tokens(shape.N) * 2 * sizeof(float));
+    total += round256((size_t)shape.B * shape.H * padded_tokens(shape.N) * 4 * sizeof(float));
   return total;
 }
 
@@ -388,7 +388,7 @@ mxattn_status mxattn_quantize_reference_modes(const void* q, const void* k, cons
 size_t mxattn_p_diagnostics_workspace_bytes(mxattn_shape shape) {
   if (check_shape(shape) != MXATTN_OK) return 0;
   return 2 * (round256(codes_bytes(shape, 0)) + round256(scales_bytes(shape, 0))) +
-         round256((size_t)shape.B * shape.H * padded_tokens(shape.N) * 2 * sizeof(float));
+         round256((size_t)shape.B * shape.H * padded_tokens(shape.N) * 4 * sizeof(float));
 }
 
 mxattn_status mxattn_p_diagnostics(const void* q, const void* k, int32_t dtype, mxattn_shape shape,

@@ -330,8 +330,28 @@ struct RowState {
   float mc;   // m * c + off
   float mcL;  // mc + log2(7.25): the fused UOS block-scale offset
   float off;  // POSTNORM: log2 l* (P = exp(s - m*) / l*); otherwise 0
-  float l;    // DIRECT / STATS: running sum of unquantized exponentials
+  float l;    // DIRECT: running sum of unquantized exponentials
+  // STATS: the row's exponentials split at the running maximum, l = cnt + sig:
+  // cnt keys at it (each exp(0) = 1 exactly) and the mass sig of the keys
+  // below it, so that rho = l - 1 = (cnt - 1) + sig keeps its relative
+  // precision however small it is.  POSTNORM / DIAG read rho back.
+  float cnt;
+  float sig;
+  float rho;
 };
+
+// OCP exponent floor(log2(x)) - 2 of a block whose maximum is the row
+// maximum's element, x = gamma_f / l* with l* = 1 + rho and gamma_f in [1, 2)
+// (1 for the post-normalized P).  While rho < 1, x lies in (1/2, 2) and
+// x >= 1 exactly when gamma_f - 1 >= rho, a comparison of two binary32 values
+// with no rounding (gamma_f - 1 is exact): the decision at the boundary x = 1
+// is exact, as P = 1/l* < 1 whenever any other key has mass.  Beyond, the
+// binary32 quotient decides.
+__device__ __forceinline__ int ocp_exponent_at_row_max(float gamma_f, float rho) {
+  if (rho < 1.0f) return (gamma_f - 1.0f >= rho) ? -2 : -3;
+  const float x = gamma_f / (1.0f + rho);
+  return (int)(__float_as_uint(x) >> 23) - 129;  // x is a normal binary32 in (0, 1)
+}
 
 template <int D, int MODE, int RULE>
 struct FwdConsts {
@@ -360,6 +380,11 @@ __device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, 
   int e;
   if constexpr (F::kExactArg) {
     e = scale_exponent<RULE>(__builtin_amdgcn_exp2f(fmaf(bmax - rs.m, F::kC, -rs.off)));
+    // post-normalized P at the row maximum is 1/l*, below 1 exactly when
+    // rho = l* - 1 > 0; OCP has a scale boundary at 1, so that block's
+    // exponent is decided from rho, not from the rounded exp2(-log2 l*)
+    if constexpr (MODE == kModePostnorm && RULE == kRuleOcp)
+      if (bmax == rs.m) e = ocp_exponent_at_row_max(1.0f, rs.rho);
   } else {
     // UOS in the log domain: e = ceil(log2(Mb) - log2(7.25)) with
     // log2(Mb) = bmax c - m c, the same argument the exponentials use; its
@@ -418,7 +443,11 @@ template <int D, int RULE>
 __device__ __forceinline__ void diag_block(const v16f& s0, const v16f& s1, float bmax, const RowState& rs,
                                            float gamma_f, float inv_gamma_f, float (&dg)[6]) {
   using F = FwdConsts<D, kModeDiag, RULE>;
-  const int e = scale_exponent<RULE>(__builtin_amdgcn_exp2f(fmaf(bmax - rs.m, F::kC, -rs.off)) * gamma_f);
+  int e = scale_exponent<RULE>(__builtin_amdgcn_exp2f(fmaf(bmax - rs.m, F::kC, -rs.off)) * gamma_f);
+  // gamma_f P at the row maximum is gamma_f / l*: at OCP's scale boundary
+  // gamma_f / l* = 1 the exponent is decided exactly from rho = l* - 1
+  if constexpr (RULE == kRuleOcp)
+    if (bmax == rs.m) e = ocp_exponent_at_row_max(gamma_f, rs.rho);
   const float nb = -(rs.off + (float)e);
   const float fe = (float)e;
   float gsum = 0.0f, cz = 0.0f, cs = 0.0f, cd = 0.0f, cu = 0.0f, ent = 0.0f;
@@ -638,8 +667,10 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
   keep_live(tmax, (int)ksw.x, (int)ksw.y, one_sc, qsc);
   keep_live(tmax, held[0], held[1], held[2], held[3]);
   float a = 1.0f;
+  bool moved = false;  // the running maximum rose in this tile
   if constexpr (!F::kFixedM) {
     const float m_new = fmaxf(rs.m, pair_max(tmax));
+    moved = m_new > rs.m;
     if (m_new != -INFINITY) {
       a = __builtin_amdgcn_exp2f((rs.m - m_new) * F::kC);  // 0 on the first visited tile
       rs.m = m_new;
@@ -648,12 +679,26 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
     }
   }
   if constexpr (MODE == kModeStats) {
-    float sum = 0.0f;
+    // keys below the (new) running maximum add their exponentials to sig,
+    // keys at it count one each; invisible keys (-inf) add nothing
+    float sum = 0.0f, cnt = 0.0f;
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sum += __builtin_amdgcn_exp2f((s[t][e] - rs.m) * F::kC);
-    rs.l = a * rs.l + pair_sum(sum);
+      for (int e = 0; e < 16; ++e) {
+        const float v = s[t][e];
+        if (v < rs.m) sum += __builtin_amdgcn_exp2f((v - rs.m) * F::kC);
+        else if (v == rs.m) cnt += 1.0f;
+      }
+    sum = pair_sum(sum);
+    cnt = pair_sum(cnt);
+    if (moved) {  // every earlier key now lies below the maximum
+      rs.sig = a * (rs.cnt + rs.sig) + sum;
+      rs.cnt = cnt;
+    } else {
+      rs.sig += sum;
+      rs.cnt += cnt;
+    }
   } else if constexpr (MODE == kModeDiag) {
     __builtin_amdgcn_sched_barrier(0);
     diag_block<D, RULE>(s[0], s[1], bmax[0], rs, gamma_f, inv_gamma_f, dg);
@@ -760,11 +805,15 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
   rs.mcL = 0.0f;
   rs.off = 0.0f;
   rs.l = 0.0f;
+  rs.cnt = 0.0f;
+  rs.sig = 0.0f;
+  rs.rho = 0.0f;
   if constexpr (F::kFixedM) {
-    const float* st = p.stats + qrow * 2;
-    rs.m = st[0];
-    rs.off = __builtin_amdgcn_logf(st[1]);  // log2 of l*
-    rs.mc = st[0] * F::kC + rs.off;
+    const float4 st = *reinterpret_cast<const float4*>(p.stats + qrow * 4);
+    rs.m = st.x;
+    rs.off = __builtin_amdgcn_logf(st.y);  // log2 of l*
+    rs.mc = st.x * F::kC + rs.off;
+    rs.rho = st.z;
   }
   float dg[6] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
   v16f acc[NCT];
@@ -835,11 +884,9 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
 
   // ---- epilogue
   if constexpr (MODE == kModeStats) {
-    if (g == 0) {
-      float* st2 = p.stats + qrow * 2;
-      st2[0] = rs.m;
-      st2[1] = rs.l;
-    }
+    // (m*, l* = cnt + sig, rho = l* - 1, unused): per row 16 bytes
+    if (g == 0)
+      *reinterpret_cast<float4*>(p.stats + qrow * 4) = make_float4(rs.m, rs.cnt + rs.sig, (rs.cnt - 1.0f) + rs.sig, 0.0f);
     return;
   }
   if constexpr (MODE == kModeDiag) {

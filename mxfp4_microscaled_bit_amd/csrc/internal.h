@@ -72,7 +72,7 @@ struct AttnArgs {
   float* out;        // [B, H, N, d]
   float* row_stats;  // nullable [B, H, N, 2] (m, l)
   float* row_sums;   // nullable [B, H, N]
-  float* stats_ws;   // POSTNORM, DIAG: [B, H, Np, 2] exact (m, l) of pass 1
+  float* stats_ws;   // POSTNORM, DIAG: [B, H, Np, 4] exact (m, l, l - 1, unused) of pass 1
   float* diag;       // DIAG: [B, H, N, 6]
   float gamma;       // DIAG: pre-quantization global scale of P
   // fused Q prologue (PNQ with the UOS softmax rule only): when qx is set,

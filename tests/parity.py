@@ -3,21 +3,21 @@ through the C ABI, and compare with the CPU oracle on the same inputs.
 
 Comparison rules:
   * codes and E8M0 scales of the quantizers: bit-exact;
-  * attention output: max |o - o_ref| <= ABS_TOL + allowance per element, and
-    sum |o - o_ref| / sum |o_ref| <= REL_TOL over the compared elements whose
-    result is unique (decision allowance <= ABS_TOL); elements of rows where a
-    near-threshold decision can move the output by more than ABS_TOL have two
-    correct results and are held to the per-element bound only.
+  * attention output, over every compared element:
+      max |o - o_ref| <= ABS_TOL (+ the accumulation allowance below), and
+      sum |o - o_ref| / sum |o_ref| <= REL_TOL.
     ABS_TOL = 1e-2 and REL_TOL = 1e-3 are the acceptance bounds of the target.
-    The allowance covers two ways the binary32 GPU path may legitimately
-    differ from the binary64 oracle:
-      - decision allowance: P~ quantization decisions that lie within a
-        relative margin DELTA of a rounding midpoint or a scale boundary may
-        go the other way (the oracle reports a first-order bound on the
-        resulting change of O_i, field ``amb``);
-      - accumulation allowance: the binary32 sum over T key tiles of
-        beta-weighted P^ V^ terms, bounded by (T + 4) u * absmass with
-        u = 2^-24 and absmass = sum beta P^ |v^| / l (field ``absmass``).
+    Elements may exceed ABS_TOL only where a quantization decision of P~ (or
+    P) lies within the relative margin DELTA of its threshold, so that the
+    binary32 GPU path and the binary64 oracle may legitimately take it
+    differently: such an element must stay within ABS_TOL + amb, where amb is
+    the oracle's bound on the output change when every such decision flips,
+    and such elements may sit in at most MAX_AMBIGUOUS_ROW_FRACTION of the
+    compared rows (never more than a couple of rows on small cases: one flipped
+    scale decision moves all d channels of its row).  The counts are printed.
+    The accumulation allowance covers the binary32 sum over T key tiles of
+    beta-weighted P^ V^ terms: (T + 4) u * absmass with u = 2^-24 and
+    absmass = sum beta P^ |v^| / l (field ``absmass``); it is ~1e-7 here.
 DELTA: the GPU evaluates y = exp2(fma(s, c, -(m c + e))) in binary32 from
 binary32 scores.  Its relative error against the binary64 oracle is
 ln2 * |error of the exponent argument| plus the exp2 error; with scores
@@ -39,6 +39,9 @@ ABS_TOL = 1e-2
 REL_TOL = 1e-3
 DELTA = 2.0 ** -13
 U32 = 2.0 ** -24
+MAX_AMBIGUOUS_ROW_FRACTION = 0.005  # rows that may hold elements beyond ABS_TOL (within their allowance)
+MIN_AMBIGUOUS_ROW_CAP = 2           # ... a couple of rows on small cases
+MIN_ROWSUM_COVERAGE = 0.95     # row sums are compared on at least this share of rows
 
 
 def say(*a):
@@ -103,20 +106,33 @@ def check_output(gpu, ref, label, n_tiles):
     """gpu: float array; ref: oracle dict sliced to the same elements."""
     o_ref = ref["out"]
     diff = np.abs(gpu.astype(np.float64) - o_ref)
-    allowance = ref["amb"] + (n_tiles + 4) * U32 * ref["absmass"] * 4.0
-    excess = diff - (ABS_TOL + allowance)
-    # mean-relative error over the elements whose result is unique: rows where a
-    # near-threshold decision could move the output by more than ABS_TOL have
-    # two correct results, and are held to the allowance bound only
-    unique = ref["amb"] <= ABS_TOL
-    rel = float(diff[unique].sum() / max(np.abs(o_ref[unique]).sum(), 1e-300))
-    rel_all = float(diff.sum() / max(np.abs(o_ref).sum(), 1e-300))
-    raw_max = float(diff.max())
-    n_need = int((diff > ABS_TOL).sum())
-    say(f"[{label}] max|diff|={raw_max:.3e} mean-rel={rel:.3e} (all elements {rel_all:.3e}) "
-        f"elements>1e-2={n_need} ambiguous={int((~unique).sum())}/{diff.size} "
-        f"within allowance={bool((excess <= 0).all())} max amb={float(ref['amb'].max()):.3e}")
+    acc = (n_tiles + 4) * U32 * ref["absmass"] * 4.0
+    beyond = diff > ABS_TOL + acc            # beyond the plain bar
+    excess = diff - (ABS_TOL + acc + ref["amb"])
+    n_beyond = int(beyond.sum())
+    rows_beyond = int(beyond.any(axis=-1).sum())
+    n_rows = int(np.prod(diff.shape[:-1]))
+    cap = max(MIN_AMBIGUOUS_ROW_CAP, int(MAX_AMBIGUOUS_ROW_FRACTION * n_rows))
+    rel = float(diff.sum() / max(np.abs(o_ref).sum(), 1e-300))
+    n_flagged = int((ref["amb"] > ABS_TOL).sum())
+    say(f"[{label}] max|diff|={float(diff.max()):.3e} mean-rel={rel:.3e} over {diff.size} elements; "
+        f"beyond 1e-2: {n_beyond} elements in {rows_beyond} of {n_rows} rows (cap {cap} rows); "
+        f"elements with a close decision worth >1e-2: {n_flagged}; "
+        f"max amb={float(ref['amb'].max()):.3e}")
     assert np.isfinite(gpu).all(), f"{label}: non-finite GPU output"
-    assert (excess <= 0).all(), f"{label}: max excess {float(excess.max()):.3e}"
+    assert (excess <= 0).all(), f"{label}: max excess over the decision allowance {float(excess.max()):.3e}"
+    assert rows_beyond <= cap, f"{label}: {n_beyond} elements beyond 1e-2 in {rows_beyond} rows (cap {cap})"
     assert rel <= REL_TOL, f"{label}: mean-relative error {rel:.3e}"
-    return raw_max, rel
+    return float(diff.max()), rel
+
+
+def check_row_sums(gpu_rs, ref, label, rtol=2e-4, atol=2e-4):
+    """Induced row sums of the reference modes against the oracle, on the rows
+    where no close decision can move the row by more than ABS_TOL; those rows
+    must be at least MIN_ROWSUM_COVERAGE of all compared rows."""
+    unique = ref["amb"].max(axis=-1) <= ABS_TOL
+    cov = float(unique.mean())
+    say(f"  [{label}] row sums compared on {int(unique.sum())}/{unique.size} rows ({100 * cov:.1f} %)")
+    assert cov >= MIN_ROWSUM_COVERAGE, f"{label}: row sums comparable on only {100 * cov:.1f} % of rows"
+    assert np.allclose(gpu_rs[unique], ref["rowsum"][unique], rtol=rtol, atol=atol), \
+        f"{label}: max row-sum diff {float(np.abs(gpu_rs[unique] - ref['rowsum'][unique]).max()):.3e}"
