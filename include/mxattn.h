@@ -91,7 +91,8 @@ typedef enum {
   MXATTN_ERR_MISMATCH = 6,  /* MXFP4 tensor descriptors disagree                    */
   MXATTN_ERR_WORKSPACE = 7, /* workspace missing or smaller than required           */
   MXATTN_ERR_ENUM = 8,      /* unknown axis, rule or P placement                    */
-  MXATTN_ERR_HIP = 9        /* a HIP runtime call or kernel launch failed           */
+  MXATTN_ERR_HIP = 9,       /* a HIP runtime call or kernel launch failed           */
+  MXATTN_ERR_SCRATCH = 10   /* the call needs more than the library's static scratch */
 } mxattn_status;
 
 typedef enum { MXATTN_BF16 = 0, MXATTN_FP16 = 1 } mxattn_dtype;
@@ -217,6 +218,30 @@ mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shap
                                  const int64_t* strides, int32_t axis, int32_t rotate,
                                  const double* q_values, int32_t n_q, double* sse,
                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Size of the device array, allocated once per GPU with the library's code
+ * and kept until the process ends, that mxattn_scale_sweep_noalloc uses in
+ * place of a workspace. */
+#define MXATTN_SWEEP_SCRATCH_BYTES (16u << 20)
+
+/* mxattn_scale_sweep without a workspace argument, for callers that cannot
+ * allocate device memory around the call: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  The per-workgroup
+ * partial sums go to a static device array of MXATTN_SWEEP_SCRATCH_BYTES
+ * (one per GPU, resolved on the call's current device at its first call
+ * there); the call itself allocates nothing.  Arguments, results and the
+ * other errors are those of mxattn_scale_sweep; the result is bit-identical
+ * to it.  MXATTN_ERR_SCRATCH if mxattn_scale_sweep_workspace_bytes(shape,
+ * axis, n_q) exceeds MXATTN_SWEEP_SCRATCH_BYTES (e.g. B*H = 40, N = 32760,
+ * d = 128 with 48 boundaries needs 1.97 MB; the limit admits about 8x that),
+ * and nothing is enqueued.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * give undefined sums; order them.  Nothing in the array needs clearing:
+ * every partial sum is written before it is read. */
+mxattn_status mxattn_scale_sweep_noalloc(const void* x, int32_t dtype, mxattn_shape shape,
+                                         const int64_t* strides, int32_t axis, int32_t rotate,
+                                         const double* q_values, int32_t n_q, double* sse,
+                                         hipStream_t stream);
 
 /* Fused MXFP4 attention forward with PNQ (Alg. 2).
  *   q        head-dimension MXFP4 tensor, shape [B, H, Nq, d]

@@ -25,6 +25,7 @@ SCALE_UOS, SCALE_OCP, SCALE_CEIL_Q = 0, 1, 2
 P_PNQ, P_DIRECT, P_POSTNORM = 0, 1, 2
 TOKEN_ALIGN = 128
 SWEEP_MAX = 48
+SWEEP_SCRATCH_BYTES = 16 << 20  # MXATTN_SWEEP_SCRATCH_BYTES
 
 EXPORTED = (
     "mxattn_mx_codes_bytes",
@@ -35,6 +36,7 @@ EXPORTED = (
     "mxattn_rotate_quantize_qkv",
     "mxattn_scale_sweep_workspace_bytes",
     "mxattn_scale_sweep",
+    "mxattn_scale_sweep_noalloc",
     "mxattn_forward",
     "mxattn_forward_fused_q",
     "mxattn_reference_modes_workspace_bytes",
@@ -94,6 +96,8 @@ def lib():
     L.mxattn_scale_sweep_workspace_bytes.argtypes = [Shape, i32, i32]
     L.mxattn_scale_sweep.restype = i32
     L.mxattn_scale_sweep.argtypes = [vp, i32, Shape, vp, i32, i32, vp, i32, vp, vp, sz, vp]
+    L.mxattn_scale_sweep_noalloc.restype = i32
+    L.mxattn_scale_sweep_noalloc.argtypes = [vp, i32, Shape, vp, i32, i32, vp, i32, vp, vp]
     L.mxattn_forward.restype = i32
     L.mxattn_forward.argtypes = [ctypes.POINTER(MXTensorDesc)] * 3 + [i32, vp, vp, vp]
     L.mxattn_reference_modes_workspace_bytes.restype = sz
@@ -318,6 +322,26 @@ def scale_sweep(x: torch.Tensor, q_values, axis: int = AXIS_HEAD_DIM, rotate: bo
                                         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
                                         workspace.numel() * workspace.element_size(), _stream(stream, dev)),
                "mxattn_scale_sweep")
+    return out
+
+
+def scale_sweep_noalloc(x: torch.Tensor, q_values, axis: int = AXIS_HEAD_DIM, rotate: bool = True,
+                        out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """mxattn_scale_sweep_noalloc: scale_sweep with the library's static scratch
+    in place of a workspace (the library allocates nothing; pass `out` to
+    allocate nothing here either).  Returns float64 [B*H, len(q_values)]."""
+    B, H, N, d = x.shape
+    dev = _device(x)
+    qs = (ctypes.c_double * len(q_values))(*[float(q) for q in q_values])
+    if out is None:
+        out = torch.empty((B * H, len(q_values)), dtype=torch.float64, device=dev)
+    _device(x, out)
+    _buffer(out, B * H * len(q_values) * 8, "out")
+    with torch.cuda.device(dev):
+        _check(lib().mxattn_scale_sweep_noalloc(ctypes.c_void_p(x.data_ptr()), _dtype_enum(x), _shape(B, H, N, d),
+                                                _strides(x), axis, int(bool(rotate)), qs, len(q_values),
+                                                ctypes.c_void_p(out.data_ptr()), _stream(stream, dev)),
+               "mxattn_scale_sweep_noalloc")
     return out
 
 

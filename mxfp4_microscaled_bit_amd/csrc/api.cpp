@@ -244,10 +244,11 @@ size_t mxattn_scale_sweep_workspace_bytes(mxattn_shape shape, int32_t axis, int3
   return round256((size_t)shape.B * shape.H * sweep_chunks(axis, shape.N, shape.d) * n_q * sizeof(double));
 }
 
-mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shape,
-                                 const int64_t* strides, int32_t axis, int32_t rotate,
-                                 const double* q_values, int32_t n_q, double* sse,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+// Validation shared by the two sweep entry points; fills everything of `a`
+// but the partial-sum buffer.
+static mxattn_status sweep_args(const void* x, int32_t dtype, mxattn_shape shape, const int64_t* strides,
+                                int32_t axis, int32_t rotate, const double* q_values, int32_t n_q, double* sse,
+                                SweepArgs& a) {
   if (!x || !q_values || !sse) return MXATTN_ERR_NULL;
   if (dtype != MXATTN_BF16 && dtype != MXATTN_FP16) return MXATTN_ERR_DTYPE;
   if (axis != MXATTN_AXIS_HEAD_DIM && axis != MXATTN_AXIS_TOKEN) return MXATTN_ERR_ENUM;
@@ -265,11 +266,6 @@ mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shap
   int64_t s[3];
   st = resolve_strides(shape, strides, s);
   if (st != MXATTN_OK) return st;
-  const size_t need = mxattn_scale_sweep_workspace_bytes(shape, axis, n_q);
-  if (!workspace || workspace_bytes < need) return MXATTN_ERR_WORKSPACE;
-  if (!aligned16(x) || !aligned16(sse) || !aligned16(workspace)) return MXATTN_ERR_ALIGN;
-
-  SweepArgs a;
   a.x = x;
   a.dtype = dtype;
   a.B = shape.B; a.H = shape.H; a.N = shape.N; a.d = shape.d;
@@ -280,9 +276,36 @@ mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shap
   for (int j = 0; j < n_q; ++j) a.qbits[j] = boundary_bits(q_values[j]);
   a.qmin_bits = boundary_bits(qmin);
   a.chunks = sweep_chunks(axis, shape.N, shape.d);
-  a.partial = static_cast<double*>(workspace);
+  a.partial = nullptr;
   a.sse = sse;
+  return MXATTN_OK;
+}
+
+mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shape,
+                                 const int64_t* strides, int32_t axis, int32_t rotate,
+                                 const double* q_values, int32_t n_q, double* sse,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  SweepArgs a;
+  mxattn_status st = sweep_args(x, dtype, shape, strides, axis, rotate, q_values, n_q, sse, a);
+  if (st != MXATTN_OK) return st;
+  const size_t need = mxattn_scale_sweep_workspace_bytes(shape, axis, n_q);
+  if (!workspace || workspace_bytes < need) return MXATTN_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(sse) || !aligned16(workspace)) return MXATTN_ERR_ALIGN;
+  a.partial = static_cast<double*>(workspace);
   return hip_status(launch_scale_sweep(a, stream));
+}
+
+mxattn_status mxattn_scale_sweep_noalloc(const void* x, int32_t dtype, mxattn_shape shape,
+                                         const int64_t* strides, int32_t axis, int32_t rotate,
+                                         const double* q_values, int32_t n_q, double* sse,
+                                         hipStream_t stream) {
+  SweepArgs a;
+  mxattn_status st = sweep_args(x, dtype, shape, strides, axis, rotate, q_values, n_q, sse, a);
+  if (st != MXATTN_OK) return st;
+  if (mxattn_scale_sweep_workspace_bytes(shape, axis, n_q) > (size_t)MXATTN_SWEEP_SCRATCH_BYTES)
+    return MXATTN_ERR_SCRATCH;
+  if (!aligned16(x) || !aligned16(sse)) return MXATTN_ERR_ALIGN;
+  return hip_status(launch_scale_sweep_static(a, stream));
 }
 
 
@@ -451,6 +474,7 @@ const char* mxattn_status_string(mxattn_status status) {
     case MXATTN_ERR_WORKSPACE: return "workspace missing or too small";
     case MXATTN_ERR_ENUM: return "unknown axis, rule, placement or flag value";
     case MXATTN_ERR_HIP: return "HIP runtime error";
+    case MXATTN_ERR_SCRATCH: return "problem exceeds the library's static scratch (MXATTN_SWEEP_SCRATCH_BYTES)";
   }
   return "unknown status";
 }

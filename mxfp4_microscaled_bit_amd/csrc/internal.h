@@ -49,6 +49,10 @@ struct SweepArgs {
 
 int sweep_chunks(int axis, int N, int d);
 hipError_t launch_scale_sweep(const SweepArgs& a, hipStream_t stream);
+// The same with a.partial ignored: the partial sums go to the library's
+// static per-GPU scratch array (the caller has checked the size against
+// MXATTN_SWEEP_SCRATCH_BYTES).
+hipError_t launch_scale_sweep_static(const SweepArgs& a, hipStream_t stream);
 
 enum AttnMode : int {
   kModePnq = 0,

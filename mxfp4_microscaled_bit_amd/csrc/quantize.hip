@@ -30,9 +30,19 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "internal.h"
 #include "mx_block.h"
+#include "mxattn.h"
 #include "quant_index.h"
+
+// Partial sums of mxattn_scale_sweep_noalloc: one array per GPU, created with
+// the library's code object on that device and kept until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: host
+// code reaches the array only through the address hipGetSymbolAddress returns
+// for the current device (sweep_scratch_ptr below).
+static __device__ __align__(256) double scratch[MXATTN_SWEEP_SCRATCH_BYTES / sizeof(double)];
 
 namespace mxattn_internal {
 namespace {
@@ -508,6 +518,37 @@ hipError_t launch_quantize_qkv(const QuantArgs& q, const QuantArgs& k, const Qua
 int sweep_chunks(int axis, int N, int d) {
   const int64_t units = axis == 1 ? (int64_t)((N + 31) / 32) * (d / 2) : (int64_t)N * (d / 32);
   return (int)((units + 256 * kSweepUnits - 1) / (256 * kSweepUnits));
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// Device address of this device's `scratch`, looked up once per device with
+// that device current (the caller's current device is the launch device).
+hipError_t sweep_scratch_ptr(double** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return err;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return err;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = static_cast<double*>(g_scratch_ptr[dev]);
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_scale_sweep_static(const SweepArgs& a, hipStream_t stream) {
+  SweepArgs b = a;
+  hipError_t err = sweep_scratch_ptr(&b.partial);
+  if (err != hipSuccess) return err;
+  return launch_scale_sweep(b, stream);
 }
 
 hipError_t launch_scale_sweep(const SweepArgs& a, hipStream_t stream) {

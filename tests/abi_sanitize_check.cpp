@@ -30,6 +30,7 @@ int sweep_chunks(int axis, int N, int d) {
   return (int)((units + 1023) / 1024);
 }
 hipError_t launch_scale_sweep(const SweepArgs&, hipStream_t) { return reached("launch_scale_sweep"); }
+hipError_t launch_scale_sweep_static(const SweepArgs&, hipStream_t) { return reached("launch_scale_sweep_static"); }
 hipError_t launch_attention(const AttnArgs&, hipStream_t) { return reached("launch_attention"); }
 }  // namespace mxattn_internal
 
@@ -91,6 +92,30 @@ int main() {
          "sweep workspace");
   expect(mxattn_scale_sweep(F, 0, ok, nullptr, 0, 1, qs, 1000, sse, F, 1 << 20, nullptr), MXATTN_ERR_ENUM,
          "sweep count");
+  // the allocation-free sweep: the same validation, then the static scratch limit
+  expect(mxattn_scale_sweep_noalloc(F, 0, ok, nullptr, 0, 1, qs, 3, sse, nullptr), MXATTN_ERR_ENUM,
+         "noalloc sweep boundary spread");
+  expect(mxattn_scale_sweep_noalloc(F, 0, ok, nullptr, 0, 1, qs, 1000, sse, nullptr), MXATTN_ERR_ENUM,
+         "noalloc sweep count");
+  expect(mxattn_scale_sweep_noalloc(nullptr, 0, ok, nullptr, 0, 1, qs, 2, sse, nullptr), MXATTN_ERR_NULL,
+         "noalloc sweep input");
+  expect(mxattn_scale_sweep_noalloc(F, 7, ok, nullptr, 0, 1, qs, 2, sse, nullptr), MXATTN_ERR_DTYPE,
+         "noalloc sweep dtype");
+  expect(mxattn_scale_sweep_noalloc(F, 0, ok, nullptr, 1, 1, qs, 2, sse, nullptr), MXATTN_ERR_ENUM,
+         "noalloc sweep rotation along tokens");
+  {
+    const mxattn_shape big = {64, 64, 118800, 128};  // 731 MB of partial sums with 48 boundaries
+    double q48[48];
+    for (int j = 0; j < 48; ++j) q48[j] = 6.0 + 0.04 * j;
+    expect(mxattn_scale_sweep_noalloc(F, 0, big, nullptr, 0, 1, q48, 48, sse, nullptr), MXATTN_ERR_SCRATCH,
+           "noalloc sweep beyond the static scratch");
+    if (mxattn_scale_sweep_workspace_bytes(big, 0, 48) <= (size_t)MXATTN_SWEEP_SCRATCH_BYTES) {
+      fprintf(stderr, "the oversize case fits the scratch\n");
+      ++failures;
+    }
+  }
+  expect(mxattn_scale_sweep_noalloc(F + 1, 0, ok, nullptr, 0, 1, qs, 2, sse, nullptr), MXATTN_ERR_ALIGN,
+         "noalloc sweep alignment");
 
   mxattn_mx_tensor q = {F, F, ok, MXATTN_AXIS_HEAD_DIM, 0, 1}, k = q, v = q;
   v.axis = MXATTN_AXIS_TOKEN;
