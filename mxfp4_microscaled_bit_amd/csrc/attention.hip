@@ -52,6 +52,7 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
 constexpr int kBr = 128;       // queries per workgroup
+constexpr int kThreads = 256;  // threads per workgroup
 constexpr int kBc = kKvTile;   // keys per tile
 constexpr int kRuleUos = 0;
 constexpr int kRuleOcp = 1;
@@ -190,8 +191,10 @@ struct ScaleRegs {
   uint32_t vs;
 };
 
-// thread k < 128 loads the d/32 scale bytes of key k; thread j < d loads
-// scale bytes 4j..4j+3 of the tile's [block][channel] V^ scales
+// Thread k < 128 (waves 0-1) loads the d/32 scale bytes of key k; the last
+// d threads (waves 2-3 at d = 128), j = tid - (256 - d), load scale bytes
+// 4j..4j+3 of the tile's [block][channel] V^ scales: the staging work is
+// split between the waves, which meet at every tile's barrier.
 template <int D>
 __device__ __forceinline__ ScaleRegs scale_load(const Params& p, int64_t bh, int kt, int tid) {
   const int NBp = p.Np / 32;
@@ -202,9 +205,9 @@ __device__ __forceinline__ ScaleRegs scale_load(const Params& p, int64_t bh, int
     if constexpr (D == 128) r.ks = __builtin_amdgcn_raw_buffer_load_b32(kr, 4 * tid, 0, 0);
     else r.ks = __builtin_amdgcn_raw_buffer_load_b16(kr, 2 * tid, 0, 0);
   }
-  if (tid < D) {
+  if (tid >= kThreads - D) {
     const __amdgpu_buffer_rsrc_t vr = tile_rsrc(p.vs + (bh * NBp + (int64_t)kt * 4) * D, 4 * D);
-    r.vs = __builtin_amdgcn_raw_buffer_load_b32(vr, 4 * tid, 0, 0);
+    r.vs = __builtin_amdgcn_raw_buffer_load_b32(vr, 4 * (tid - (kThreads - D)), 0, 0);
   }
 #endif
   return r;
@@ -233,12 +236,13 @@ __device__ __forceinline__ void scale_store(const ScaleRegs& sr, uint8_t* stage,
       base[8 * (r + 32) + (t & 1)] = (uint8_t)((s >> 8) & 0xFFu);
     }
   }
-  if (tid < D) {
-    const int bl = (4 * tid) / D, ch0 = (4 * tid) % D;
+  if (tid >= kThreads - D) {
+    const int j = tid - (kThreads - D);
+    const int bl = (4 * j) / D, ch0 = (4 * j) % D;
     const int lane0 = 32 * (bl & 1) + (ch0 & 31);
     uint8_t* base = stage + L::VS + 4 * (bl >> 1) + (ch0 >> 5);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) base[8 * (lane0 + j)] = (uint8_t)(sr.vs >> (8 * j));
+    for (int i = 0; i < 4; ++i) base[8 * (lane0 + i)] = (uint8_t)(sr.vs >> (8 * i));
   }
 }
 
@@ -377,7 +381,8 @@ __device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, 
                                                 int& psc, float& lpart) {
   using F = FwdConsts<D, MODE, RULE>;
   // block scale from the block max of the exponentials (exp is monotone)
-  int e;
+  int e = 0;
+  float ef = 0.0f;
   if constexpr (F::kExactArg) {
     e = scale_exponent<RULE>(__builtin_amdgcn_exp2f(fmaf(bmax - rs.m, F::kC, -rs.off)));
     // post-normalized P at the row maximum is 1/l*, below 1 exactly when
@@ -392,7 +397,7 @@ __device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, 
     // margin of the exp2 evaluation.  A fully masked block (-inf) takes the
     // clamp; its elements are all zero whatever the scale.
     // (bmax <= m, so e <= ceil(-log2 7.25) = -2: no upper clamp)
-    e = (int)__builtin_ceilf(fmaxf(fmaf(bmax, F::kC, -rs.mcL), -127.0f));
+    ef = __builtin_ceilf(fmaxf(fmaf(bmax, F::kC, -rs.mcL), -127.0f));
   }
   float y[32];
   if constexpr (F::kExactArg) {
@@ -403,7 +408,7 @@ __device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, 
       y[16 + k] = __builtin_amdgcn_exp2f(fmaf(s1[k] - rs.m, F::kC, nb));
     }
   } else {
-    const float nb = -(rs.mc + (float)e);
+    const float nb = -(rs.mc + ef);
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
       y[k] = __builtin_amdgcn_exp2f(fmaf(s0[k], F::kC, nb));
@@ -416,7 +421,10 @@ __device__ __forceinline__ uint4 quantize_block(const v16f& s0, const v16f& s1, 
     for (int k = 0; k < 32; ++k) sum += y[k];
     lpart = __builtin_amdgcn_ldexpf(sum, e);
   }
-  psc = e + 127;
+  // the E8M0 byte: e + 127 as the low byte of ef + (1.5 2^23 + 127) (an
+  // exact sum; the products read only byte 0 of their scale registers)
+  if constexpr (F::kExactArg) psc = e + 127;
+  else psc = __float_as_int(ef + 12583039.0f);
   return make_uint4(pack_fp4x8(y), pack_fp4x8(y + 8), pack_fp4x8(y + 16), pack_fp4x8(y + 24));
 }
 
@@ -509,9 +517,9 @@ __device__ __forceinline__ void mask_scores(v16f (&s)[4], int kt, int N, int q, 
 // one running chain, which the compiler turns into v_max3_f32 (two new
 // elements per instruction)
 __device__ __forceinline__ float max32(const v16f& a, const v16f& b) {
-  float m = a[0];
+  float m = -INFINITY;
 #pragma unroll
-  for (int k = 1; k < 16; ++k) m = fmaxf(m, a[k]);
+  for (int k = 0; k < 16; ++k) m = fmaxf(m, a[k]);
 #pragma unroll
   for (int k = 0; k < 16; ++k) m = fmaxf(m, b[k]);
   return m;
