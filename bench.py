@@ -16,6 +16,14 @@ plain CPU oracle on a bounded sample of the same workload.  `accuracy` gives
 the error of the output against fp32 softmax attention on the unquantized
 inputs (PyTorch on the GPU, sampled rows, outside the timed region).
 
+After the timed steps, in-run probes (libmxprobe.so) measure what this GPU
+reaches at its current clock and power state: dense scaled-FP4 matrix
+products, the forward's vector work per (query, key) pair (one FMA, one
+v_exp_f32, half an FP4 convert, half a max3, at two waves per SIMD) and a
+16-byte copy's read+write bandwidth.  `roofline_valu` prices the forward
+against the vector-mix probe; `forward` and `quantizer` also give their
+fractions against the matrix and copy probes.
+
 With --separate-quantize the three tensors are quantized by three
 mxattn_rotate_quantize launches, and the JSON line adds per-launch rates for K
 and V.  With --fused-q the step quantizes K and V (two launches) and runs the
@@ -23,7 +31,7 @@ forward entry point that rotates and quantizes Q in its own prologue (no Q^
 buffer).
 
     python bench.py [--steps K] [--warmup W] [--workload 2] [--separate-quantize] [--fused-q]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--no-probes]
 """
 from __future__ import annotations
 
@@ -72,6 +80,17 @@ def measured_traffic(launch_bytes_algorithmic: float):
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, target_s: float = 15.0):
     """The CPU oracle on a bounded sample of the workload: query rows of a few
     heads, each row against all N keys, sized to about target_s seconds (the
@@ -114,6 +133,7 @@ def cpu_baseline(w, target_s: float = 15.0):
         "value": flops / t / 1e12,
         "unit": "TFLOPS",
         "cores": nth,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "seconds": round(t, 3),
         "sample": (f"{n_heads} heads x {n_rows} query rows x all {w.N} keys of {w.name} "
@@ -167,6 +187,7 @@ def main():
                     help="quantize Q, K and V with three mxattn_rotate_quantize launches instead of one "
                          "mxattn_rotate_quantize_qkv launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probes", action="store_true", help="skip the in-run throughput probes")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run three plain device-to-device copies of BYTES bytes and exit "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -274,6 +295,8 @@ def main():
     fwd_ms = sum(e[3].elapsed_time(e[4]) for e in events) / len(events)
     ms_per_step = wall * 1000.0 / args.steps
     flops = w.flops()
+    pairs = flops / (4.0 * d)  # visible (query, key) pairs of one forward
+    traffic = measured_traffic(flops) if args.workload == 2 and not args.fused_q else None
     value = flops / (ms_per_step * 1e-3) / 1e12
     fwd_tflops = flops / (fwd_ms * 1e-3) / 1e12
     quant_bytes = B * H * ((0 if args.fused_q else N) + 2 * Nk) * d * QUANT_BYTES_PER_ELEMENT
@@ -317,9 +340,43 @@ def main():
                           "quantize_v": per_launch(v_ms, B * H * Nk * d)} if separate else {})},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_FP4_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_FP4_PEAK_TFLOPS, 4),
-                     "traffic": measured_traffic(flops) if args.workload == 2 and not args.fused_q else None},
+                     "traffic": traffic,
+                     "traffic_source": (f"stored: {os.path.relpath(TRAFFIC_FILE, ROOT)} (rocprofv3 FETCH_SIZE and "
+                                        f"WRITE_SIZE of this kernel source, sha256 {kernel_source_hash()})"
+                                        if traffic is not None else None)},
     }
     result["accuracy"] = accuracy_vs_fp32(w, dev, out)
+    if not args.no_probes:
+        from mxfp4_microscaled_bit_amd import probes
+
+        log("running the in-run throughput probes")
+        del dev
+        torch.cuda.empty_cache()
+        mfma = max(probes.mfma_fp4_tflops(groups=g) for g in (256, 512))
+        mix = probes.pair_mix_gpairs()
+        copy = probes.stream_gbs()
+        read = probes.read_gbs()
+        fwd_gpairs = pairs / (fwd_ms * 1e-3) / 1e9
+        result["probes"] = {
+            "mfma_fp4_tflops": round(mfma, 1),
+            "pair_mix_gpair_per_s": round(mix, 1),
+            "copy_read_write_gb_per_s": round(copy, 1),
+            "read_gb_per_s": round(read, 1),
+            "note": "measured in this run after the timed steps; the matrix probe runs four independent "
+                    "32x32x64 FP4 accumulators per wave, the mix probe the forward's per-pair vector work at "
+                    "two waves per SIMD, the copy probe 16-byte elements read and written, the read probe "
+                    "16-byte elements read",
+        }
+        result["forward"]["frac_mfma_probe"] = round(fwd_tflops / mfma, 4)
+        result["quantizer"]["frac_copy_probe"] = round(quant_gbs / copy, 4)
+        result["quantizer"]["frac_read_probe"] = round(quant_gbs / read, 4)
+        result["roofline_valu"] = {
+            "bound": "alu", "achieved": round(fwd_gpairs, 2), "peak": round(mix, 2), "unit": "Gpair/s",
+            "frac": round(fwd_gpairs / mix, 4), "traffic": None,
+            "peak_source": "in-run probe of the per-pair vector work (1 v_fma_f32, 1 v_exp_f32, 1/2 "
+                           "v_cvt_scalef32_pk_fp4_f32, 1/2 v_max3_f32) on every SIMD at two waves per SIMD",
+            "pairs_per_launch": pairs,
+        }
     if not args.no_cpu_baseline and Nk == N and not w.causal:
         log("timing the CPU oracle on a bounded sample")
         result["cpu_baseline"] = cpu_baseline(w)

@@ -24,6 +24,9 @@ SOURCES = {
     "attention.hip": [],
     "api.cpp": [],
 }
+# in-run throughput probes of the benchmark: a library of their own
+PROBE_SOURCES = {"probes.hip": []}
+PROBE_LIB = os.path.join(HERE, "libmxprobe.so")
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
@@ -47,18 +50,24 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda kv: _compile(*kv), SOURCES.items()))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool):
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print("built", LIB)
+        print("built", lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = list(SOURCES.items()) + list(PROBE_SOURCES.items())
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = dict(zip([k for k, _ in jobs], ex.map(lambda kv: _compile(*kv), jobs)))
+    _link([objs[k] for k in SOURCES], LIB, verbose)
+    _link([objs[k] for k in PROBE_SOURCES], PROBE_LIB, verbose)
     return LIB
 
 

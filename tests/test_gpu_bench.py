@@ -39,6 +39,30 @@ def test_bench_json_line():
     assert d["config"]["quantizer_launches"] == 1 and "rotate_quantize_k" not in q
     a = d["accuracy"]
     assert -1.0 <= a["mean_row_cosine"] <= 1.0 and a["max_abs"] >= 0
+    # in-run probes and the vector-unit roofline priced against them
+    p = d["probes"]
+    assert p["mfma_fp4_tflops"] > 0 and p["pair_mix_gpair_per_s"] > 0 and p["copy_read_write_gb_per_s"] > 0
+    rv = d["roofline_valu"]
+    assert rv["bound"] == "alu" and rv["unit"] == "Gpair/s" and abs(rv["peak"] - p["pair_mix_gpair_per_s"]) < 0.1
+    assert abs(rv["frac"] - rv["achieved"] / rv["peak"]) < 1e-3
+    assert rv["pairs_per_launch"] == 1 * 2 * 256 * 256  # B H N Nk of the tiny workload
+    assert d["forward"]["frac_mfma_probe"] > 0 and d["quantizer"]["frac_copy_probe"] > 0
+
+
+@pytest.mark.gpu
+def test_bench_probes_measure_plausible_rates():
+    """The probes on their own: the dense FP4 matrix rate is within the
+    published 10.1 PFLOP/s (and above a third of it), the copy bandwidth
+    within the 8 TB/s HBM peak."""
+    sys.path.insert(0, ROOT)
+    from mxfp4_microscaled_bit_amd import probes
+    mfma = probes.mfma_fp4_tflops(groups=256, iters=500)
+    copy = probes.stream_gbs(nbytes=256 << 20)
+    read = probes.read_gbs(nbytes=256 << 20)
+    mix = probes.pair_mix_gpairs(iters=200)
+    assert 3000 < mfma < 10100 * 1.02, mfma
+    assert 500 < copy < 8000 and 500 < read < 8000, (copy, read)
+    assert mix > 0
 
 
 @pytest.mark.gpu
