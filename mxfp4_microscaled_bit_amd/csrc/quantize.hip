@@ -217,9 +217,15 @@ __global__ __launch_bounds__(256) void k_quantize_tokens(QTensor t, uint32_t qb)
 // Q, K and V of one attention call in one launch: workgroups [0, gq) quantize
 // Q and [gq, gq + gk) K along d (rotated if ROTATE), the rest V along tokens.
 // One launch instead of three saves two kernel boundaries, where the GPU
-// drains one grid before the next one fills it.
+// drains one grid before the next one fills it.  With both code paths in one
+// function the compiler allocated 105 VGPRs (four waves per SIMD) although
+// neither path needs more than the token path's 71 on its own; the bound of
+// seven waves per SIMD (at most 72 VGPRs, no spills; eight would spill)
+// restores the standalone kernels' memory parallelism.  Measured on the
+// MI355X, interleaved, identical codes: Wan-like 230 vs 241 us, Hunyuan-like
+// 491 vs 504 us.
 template <int D, int DTYPE, bool ROTATE, int RULE>
-__global__ __launch_bounds__(256) void k_quantize_qkv(QTensor q, QTensor k, QTensor v, int64_t gq, int64_t gk,
+__global__ __launch_bounds__(256, 7) void k_quantize_qkv(QTensor q, QTensor k, QTensor v, int64_t gq, int64_t gk,
                                                       uint32_t qb) {
   const int64_t g = blockIdx.x;
   if (g < gq) headdim_group<D, DTYPE, ROTATE, RULE>(q, qb, g);
