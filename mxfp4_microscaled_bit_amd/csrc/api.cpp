@@ -318,6 +318,7 @@ mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* 
   if (st != MXATTN_OK) return st;
   AttnArgs a = forward_args(q->shape, k, v, causal, out, row_stats);
   a.qc = q->codes; a.qs = q->scales;
+  a.resident_ok = 1;
   return hip_status(launch_attention(a, stream));
 }
 

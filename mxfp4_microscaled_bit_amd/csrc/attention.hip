@@ -41,8 +41,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <atomic>
+
 #include "internal.h"
 #include "mx_block.h"
+#include "row_divide.h"
 
 namespace mxattn_internal {
 namespace {
@@ -765,10 +769,96 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
 template <int D>
 constexpr int kLdsBytes = 2 * Lds<D>::STAGE;  // two key/value stages
 
+// Key/value tiles the resident-key kernel keeps in LDS for a whole head: at
+// two workgroups per CU, 4 x 17 KB at d = 128 and 8 x 9 KB at d = 64.
+template <int D>
+constexpr int kResidentTiles = D == 128 ? 4 : 8;
+
+// Q^ operand of one wave's 32 queries of query tile qt (B operand of S^T:
+// lane = query L%32, d-chunk 2h + L/32 in step h) and its scale bytes
+// (sb[h] = d-block 2h + L/32), kept apart until the operand is used so that
+// loading them waits for nothing
+template <int D>
+struct QOperand {
+  uint4 op[D / 64];
+  int sb[D / 64];
+  // scale register of the products: byte h = sb[h]
+  __device__ __forceinline__ int sc() const {
+    if constexpr (D == 128) return sb[0] | (sb[1] << 8);
+    else return sb[0];
+  }
+};
+
+template <int D>
+__device__ __forceinline__ void load_qoperand(const Params& p, int64_t bh, int qt, int wave, int r, int g,
+                                              QOperand<D>& q) {
+  const int64_t qrow = bh * p.Nqp + qt * kBr + 32 * wave + r;
+#pragma unroll
+  for (int h = 0; h < D / 64; ++h) {
+    q.op[h] = *reinterpret_cast<const uint4*>(p.qc + qrow * (D / 2) + 16 * (2 * h + g));
+    q.sb[h] = (int)p.qs[qrow * (D / 32) + 2 * h + g];
+  }
+}
+
+// Lane (r, g) holds channels 32 ct + 8 j + 4 g + (0..3) of its query in
+// accumulator elements 4 j .. 4 j + 3: one 16-byte store each of O~ / l,
+// rounded once (a correctly rounded division).  RECIP: through the row's
+// reciprocal when the row allows it, else element by element; the fallback
+// only rewrites registers, so the stores stay unconditional.  Both routes
+// give the same bits; the reciprocal pays where the epilogue is a large
+// share of a query tile (a short key loop: the resident-key kernel) and
+// measured no gain, or a small loss, in the streaming kernel.
+template <int D, bool RECIP>
+__device__ __forceinline__ void store_row(float* orow, const v16f (&acc)[D / 32], float l, int g) {
+  if constexpr (!RECIP) {
+#pragma unroll
+    for (int ct = 0; ct < D / 32; ++ct) {
+      const v16f& o = acc[ct];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<float4*>(orow + 32 * ct + 8 * j + 4 * g) =
+            make_float4(o[4 * j] / l, o[4 * j + 1] / l, o[4 * j + 2] / l, o[4 * j + 3] / l);
+    }
+    return;
+  }
+  uint32_t lo = 0xFFFFFFFFu;
+  float hi = 0.0f;
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct)
+#pragma unroll
+    for (int k = 0; k < 16; k += 2) {
+      lo = min(lo, min(row_divide_key(acc[ct][k]), row_divide_key(acc[ct][k + 1])));
+      hi = fmaxf(hi, fmaxf(fabsf(acc[ct][k]), fabsf(acc[ct][k + 1])));
+    }
+  const bool by_reciprocal = row_divide_by_reciprocal(l, lo, hi);
+  const float y = 1.0f / l;
+#pragma unroll
+  for (int ct = 0; ct < D / 32; ++ct) {
+    float q[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) q[k] = quotient_from_reciprocal(acc[ct][k], l, y);
+    if (!by_reciprocal) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) q[k] = acc[ct][k] / l;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<float4*>(orow + 32 * ct + 8 * j + 4 * g) =
+          make_float4(q[4 * j], q[4 * j + 1], q[4 * j + 2], q[4 * j + 3]);
+  }
+}
+
 // One query tile (128 queries of head bh): the whole online-softmax pass over
 // its key tiles and the epilogue.
-template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ>
-__device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, int64_t bh, int qt, int tid) {
+// RESIDENT: every key/value tile of the head is already in LDS, tile kt in
+// stage kt (the resident-key kernel), and the Q^ operand comes in `pre`.
+// NEXT (resident only): query tile qt + 1 of the head follows; its Q^ is
+// loaded into `pre` as this tile starts, landing under this tile's key loop,
+// and this tile's rows are all real queries, so its output stores go
+// unguarded -- the next tile's wait for its Q^ then leaves them in flight.
+template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ, bool RESIDENT = false, bool NEXT = false>
+__device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, int64_t bh, int qt, int tid,
+                                                QOperand<D>* pre = nullptr) {
   using L = Lds<D>;
   using F = FwdConsts<D, MODE, RULE>;
   constexpr int NH = D / 64;
@@ -787,11 +877,17 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
   const int64_t qrow = bh * p.Nqp + qi;
   uint4 qop[NH];
   int qsc;
-  if constexpr (!FUSEDQ) {
+  if constexpr (RESIDENT) {
 #pragma unroll
-    for (int h = 0; h < NH; ++h) qop[h] = *reinterpret_cast<const uint4*>(p.qc + qrow * (D / 2) + 16 * (2 * h + g));
-    if constexpr (D == 128) qsc = (int)p.qs[qrow * 4 + g] | ((int)p.qs[qrow * 4 + 2 + g] << 8);
-    else qsc = (int)p.qs[qrow * 2 + g];
+    for (int h = 0; h < NH; ++h) qop[h] = pre->op[h];
+    qsc = pre->sc();
+    if constexpr (NEXT) load_qoperand<D>(p, bh, qt + 1, wave, r, g, *pre);
+  } else if constexpr (!FUSEDQ) {
+    QOperand<D> q;
+    load_qoperand<D>(p, bh, qt, wave, r, g, q);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) qop[h] = q.op[h];
+    qsc = q.sc();
   }
 
   // 0/1 A operand of the l product (row L%16, K chunk L/16)
@@ -837,7 +933,9 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
   pend.psc = 127;
 
   const DmaPlan<D> plan(tid);
-  if constexpr (FUSEDQ) {
+  if constexpr (RESIDENT) {
+    // the key/value tiles are resident: no copies, no barriers
+  } else if constexpr (FUSEDQ) {
     // Q rows are loaded under the first tile's DMA, quantized into the second
     // LDS stage (free until the loop's first copy), and read back in operand
     // order; a second barrier frees that stage again
@@ -869,21 +967,32 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
   // other buffer while this one is processed (on the last iteration the
   // clamped index copies this tile again into a buffer nothing reads later)
   for (int kt = 0; kt < nfull; ++kt) {
-    const uint8_t* buf = lds + (kt & 1) * L::STAGE;
-    uint8_t* nxt = lds + ((kt + 1) & 1) * L::STAGE;
-    const int kn = min(kt + 1, nkt - 1);
-    codes_dma<D>(p, plan, bh, kn, nxt, tid);
-    const ScaleRegs sr = scale_load<D>(p, bh, kn, tid);
-    tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, one_sc, rs, acc, accl, held, lane,
-                                            koff, dg, p.gamma_f, p.inv_gamma_f, pend);
-    scale_store<D>(sr, nxt, tid);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if constexpr (RESIDENT) {
+      tile_step<D, CAUSAL, MODE, RULE, false>(lds + kt * L::STAGE, kt, p.N, qop, qsc, qi, ones, one_sc, rs, acc,
+                                              accl, held, lane, koff, dg, p.gamma_f, p.inv_gamma_f, pend);
+    } else {
+      const uint8_t* buf = lds + (kt & 1) * L::STAGE;
+      uint8_t* nxt = lds + ((kt + 1) & 1) * L::STAGE;
+      const int kn = min(kt + 1, nkt - 1);
+      codes_dma<D>(p, plan, bh, kn, nxt, tid);
+      const ScaleRegs sr = scale_load<D>(p, bh, kn, tid);
+      tile_step<D, CAUSAL, MODE, RULE, false>(buf, kt, p.N, qop, qsc, qi, ones, one_sc, rs, acc, accl, held, lane,
+                                              koff, dg, p.gamma_f, p.inv_gamma_f, pend);
+      scale_store<D>(sr, nxt, tid);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+    }
   }
   // at most one masked tile: the ragged end of the keys or the causal diagonal
-  if (nfull < nkt)
-    tile_step<D, CAUSAL, MODE, RULE, true>(lds + (nfull & 1) * L::STAGE, nfull, p.N, qop, qsc, qi, ones, one_sc, rs,
-                                           acc, accl, held, lane, koff, dg, p.gamma_f, p.inv_gamma_f, pend);
+  if (nfull < nkt) {
+    int nkeys = p.N;
+    // (resident keys: the same masks for every query tile of a run, which
+    // would otherwise be hoisted out of the run's loop into scalar registers)
+    if constexpr (RESIDENT) asm volatile("" : "+s"(nkeys));
+    tile_step<D, CAUSAL, MODE, RULE, true>(lds + (RESIDENT ? nfull : (nfull & 1)) * L::STAGE, nfull, nkeys, qop, qsc,
+                                           qi, ones, one_sc, rs, acc, accl, held, lane, koff, dg, p.gamma_f,
+                                           p.inv_gamma_f, pend);
+  }
   if constexpr (kDeferPV<D, CAUSAL> && MODE != kModeStats && MODE != kModeDiag) {
     issue_pending<D>(pend, acc, accl, ones, one_sc);  // the last tile's second half
     held[0] = pend.vsc;
@@ -925,22 +1034,13 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
   if constexpr (MODE == kModePnq) l = lsum;
   else if constexpr (MODE == kModeDirect) l = rs.l;
   else l = 1.0f;
-  // Lane (r, g) holds channels 32 ct + 8 j + 4 g + (0..3) of query qi in
-  // accumulator elements 4 j .. 4 j + 3: one 16-byte store each.  (Staging the
-  // tile through LDS into whole 128-byte row segments measured no faster on
-  // the Wan-like shape and 4-5 % slower on the causal and cross-attention
-  // shapes, whose short key loops make the epilogue a larger share.)
-  if (qi < p.Nq) {
-    float* orow = p.out + (bh * p.Nq + qi) * D;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const v16f& o = acc[ct];
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<float4*>(orow + 32 * ct + 8 * j + 4 * g) =
-            make_float4(o[4 * j] / l, o[4 * j + 1] / l, o[4 * j + 2] / l, o[4 * j + 3] / l);
-    }
-  }
+  // (Staging the tile through LDS into whole 128-byte row segments measured
+  // no faster on the Wan-like shape and 4-5 % slower on the causal and
+  // cross-attention shapes, whose short key loops make the epilogue a larger
+  // share.)
+  float* orow = p.out + (bh * p.Nq + qi) * D;
+  if constexpr (RESIDENT && NEXT) store_row<D, true>(orow, acc, l, g);  // qt + 1 < nqt: every row is a query
+  else if (qi < p.Nq) store_row<D, RESIDENT>(orow, acc, l, g);
   if (g == 0 && qi < p.Nq) {
     if (p.row_stats) {
       p.row_stats[(bh * p.Nq + qi) * 2 + 0] = rs.m * F::kInvSqrtD;
@@ -980,6 +1080,90 @@ __global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Pa
   }
 }
 
+// Resident-key forward for short key/value sequences (every tile of a head
+// fits in LDS: cross-attention against a few hundred text tokens).  The
+// B H nqt query tiles, in (head, tile) order, are dealt out in runs of
+// `per_group`, one run per workgroup, so that every workgroup has the same
+// work.  For each head its run touches, a workgroup copies the head's K^, V^
+// tiles into LDS once and then runs that head's query tiles against them
+// with no further copies or barriers.  Each query tile runs exactly the code
+// of the streaming kernel (same tiles, same order), so every output row is
+// the same bit for bit; the next query tile's Q^ is loaded before the
+// current one's output stores, which then overlap the next tile's work.
+template <int D, int MODE, int RULE>
+__global__ __launch_bounds__(256, 2) void k_attention_resident(Params p, int64_t total, int per_group) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kResidentTiles<D> * Lds<D>::STAGE];
+  const int tid = threadIdx.x;
+  const int G = gridDim.x, bid = blockIdx.x;
+  const int xcd = bid & 7, idx = bid >> 3, qx = G >> 3, rx = G & 7;
+  const int logical = (xcd < rx) ? xcd * (qx + 1) + idx : rx * (qx + 1) + (xcd - rx) * qx + idx;
+  const int64_t g0 = (int64_t)logical * per_group, g1 = min(g0 + per_group, total);
+  const int nkt = (p.N + kBc - 1) / kBc;  // <= kResidentTiles<D> (checked by the launcher)
+  const int wave = tid >> 6, lane = tid & 63;
+  const DmaPlan<D> plan(tid);
+  QOperand<D> q;
+  for (int64_t gi = g0; gi < g1;) {  // uniform over the workgroup
+    const int64_t bh = gi / p.nqt;
+    const int qt0 = (int)(gi - bh * p.nqt);
+    const int qt1 = (int)min<int64_t>(p.nqt, qt0 + (g1 - gi));
+    if (gi != g0) __syncthreads();  // every wave is done with the previous head's tiles
+    // every copy and scale load in flight before the first scale store waits
+    ScaleRegs sr[kResidentTiles<D>];
+#pragma unroll
+    for (int kt = 0; kt < kResidentTiles<D>; ++kt)
+      if (kt < nkt) {
+        codes_dma<D>(p, plan, bh, kt, lds + kt * Lds<D>::STAGE, tid);
+        sr[kt] = scale_load<D>(p, bh, kt, tid);
+      }
+#pragma unroll
+    for (int kt = 0; kt < kResidentTiles<D>; ++kt)
+      if (kt < nkt) scale_store<D>(sr[kt], lds + kt * Lds<D>::STAGE, tid);
+    load_qoperand<D>(p, bh, qt0, wave, lane & 31, lane >> 5, q);
+    __builtin_amdgcn_s_waitcnt(0);  // the head's tiles have landed in LDS
+    __syncthreads();
+    // each query tile derives its per-lane addresses afresh (t), as in the
+    // streaming kernel, rather than holding them in registers across tiles;
+    // the run's last tile has no successor and is peeled off
+    for (int qt = qt0; qt + 1 < qt1; ++qt) {
+      int t = tid;
+      asm volatile("" : "+v"(t));
+      attention_qtile<D, false, MODE, RULE, false, true, true>(p, lds, bh, qt, t, &q);
+    }
+    {
+      int t = tid;
+      asm volatile("" : "+v"(t));
+      attention_qtile<D, false, MODE, RULE, false, true, false>(p, lds, bh, qt1 - 1, t, &q);
+    }
+    gi += qt1 - qt0;
+  }
+}
+
+// Compute units of the current device, looked up once per device.
+int device_cus() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v > 0) return v;
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v < 1) v = 256;
+  cached[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+// Resident-key launch: the query tiles dealt evenly over at most one
+// workgroup per slot (two per CU).
+template <int D, int MODE, int RULE>
+hipError_t launch_resident(const Params& prm, int BH, hipStream_t stream) {
+  const int64_t slots = 2 * (int64_t)device_cus();
+  const int64_t total = (int64_t)BH * prm.nqt;
+  const int64_t per_group = (total + slots - 1) / slots;
+  const int64_t groups = (total + per_group - 1) / per_group;
+  if (per_group > 0x7FFFFFFF || groups > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_attention_resident<D, MODE, RULE>), dim3((unsigned)groups), dim3(256), 0, stream, prm, total,
+                     (int)per_group);
+  return hipGetLastError();
+}
+
 template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ = false>
 hipError_t launch_one(const Params& prm, int BH, hipStream_t stream) {
   const int64_t groups = (int64_t)BH * (CAUSAL ? (prm.nqt + 1) / 2 : prm.nqt);
@@ -992,6 +1176,11 @@ template <int D, bool CAUSAL>
 hipError_t dispatch_mode(const AttnArgs& a, const Params& prm, hipStream_t s) {
   const int BH = a.B * a.H;
   if (a.qx) return launch_one<D, CAUSAL, kModePnq, kRuleUos, true>(prm, BH, s);  // fused Q prologue
+  if constexpr (!CAUSAL) {
+    // every key/value tile of a head fits in LDS: the resident-key kernel
+    if (a.resident_ok && a.mode == kModePnq && a.rule == kRuleUos && (prm.N + kBc - 1) / kBc <= kResidentTiles<D>)
+      return launch_resident<D, kModePnq, kRuleUos>(prm, BH, s);
+  }
   if (a.mode == kModePnq && a.rule == kRuleUos) return launch_one<D, CAUSAL, kModePnq, kRuleUos>(prm, BH, s);
   if (a.mode == kModePnq) return launch_one<D, CAUSAL, kModePnq, kRuleOcp>(prm, BH, s);
   if (a.mode == kModeDirect)

@@ -84,6 +84,9 @@ struct AttnArgs {
   // inside the forward
   const void* qx = nullptr;
   int qdtype = 0;
+  // the caller allows the resident-key kernel (non-causal PNQ forward whose
+  // key/value tiles all fit in LDS); the results are the same bit for bit
+  int resident_ok = 0;
   int64_t qsB = 0, qsH = 0, qsN = 0;
   int qrotate = 0, qrule = 0;
 };
