@@ -37,6 +37,8 @@ def test_bench_json_line():
     q = d["quantizer"]
     assert q["gb_per_s"] > 0 and 0 < q["frac_hbm_peak"] < 1
     assert d["config"]["quantizer_launches"] == 1 and "rotate_quantize_k" not in q
+    # the rate comes from back-to-back launches; the in-step events are reported beside it
+    assert q["timing"].startswith("per launch over") and q["ms"] > 0 and q["ms_in_step"] > 0
     a = d["accuracy"]
     assert -1.0 <= a["mean_row_cosine"] <= 1.0 and a["max_abs"] >= 0
     # in-run probes and the vector-unit roofline priced against them
