@@ -259,8 +259,12 @@ mxattn_status mxattn_scale_sweep_noalloc(const void* x, int32_t dtype, mxattn_sh
  *   row_stats device float [B, H, Nq, 2] or NULL: (m, l) per row, with m
  *            the final running maximum of S = Q^ K^T / sqrt(d) and l the
  *            final PNQ row sum (l >= 1, App. J)
- * S, l and O~ accumulate in binary32.  The exponential tile is quantized
- * with the UOS rule whatever the rule of the inputs. */
+ * S, l and O~ accumulate in binary32; O = O~ / l is correctly rounded.  The
+ * exponential tile is quantized with the UOS rule whatever the rule of the
+ * inputs.  Without the causal mask, when every key tile of a head fits in
+ * LDS (Nk <= 512 at d = 128, <= 1024 at d = 64) the call runs a kernel that
+ * keeps each head's K^, V^ resident while it walks that head's query tiles;
+ * the result is the same, bit for bit, as the streaming kernel's. */
 mxattn_status mxattn_forward(const mxattn_mx_tensor* q, const mxattn_mx_tensor* k,
                              const mxattn_mx_tensor* v, int32_t causal, float* out,
                              float* row_stats, hipStream_t stream);
