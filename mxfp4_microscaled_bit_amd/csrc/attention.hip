@@ -1088,8 +1088,9 @@ __global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Pa
 // tiles into LDS once and then runs that head's query tiles against them
 // with no further copies or barriers.  Each query tile runs exactly the code
 // of the streaming kernel (same tiles, same order), so every output row is
-// the same bit for bit; the next query tile's Q^ is loaded before the
-// current one's output stores, which then overlap the next tile's work.
+// the same bit for bit; the next query tile's Q^ is loaded as the current
+// one starts, and the current one's output stores overlap the next tile's
+// work.
 template <int D, int MODE, int RULE>
 __global__ __launch_bounds__(256, 2) void k_attention_resident(Params p, int64_t total, int per_group) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kResidentTiles<D> * Lds<D>::STAGE];
