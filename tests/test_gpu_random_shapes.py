@@ -1,0 +1,67 @@
+"""Parity of the forward with the oracle on seeded random shapes.
+
+Twenty-four cases drawn once from a fixed seed: self-attention (causal or
+not) and cross-attention (Nq != Nk), d in {64, 128}, bf16 and fp16 inputs,
+standard normals scaled by 0.5 to 3 (from spread to peaked softmax rows), and
+token counts from 1 up to past the resident-key limit (Nk <= 512 at d = 128,
+<= 1024 at d = 64), so both forward kernels are drawn.  Every query row is
+compared with the oracle (MXAttention Alg. 2 in binary64) at the plain bar of
+tests/parity.py, and the two-call output (quantize, then forward) must equal
+the fused-Q forward's bit for bit: that one always runs the streaming kernel,
+so a case the resident-key kernel serves is checked against the streaming
+kernel too."""
+import numpy as np
+import pytest
+import torch
+
+import mxfp4_microscaled_bit_amd as mx
+import oracle
+import workloads as W
+from parity import DELTA, check_output, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+KV_TILE = 128
+
+
+def _cases(n=24, seed=20261202):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        kind = ("self", "causal", "cross")[i % 3]
+        Nq = int(rng.integers(1, 600))
+        Nk = Nq if kind != "cross" else int(rng.integers(1, 1100))
+        dtype = int(rng.choice([W.BF16, W.FP16]))
+        scale = float(rng.choice([0.5, 1.5, 3.0]))
+        out.append((i, B, H, Nq, Nk, d, kind == "causal", dtype, scale))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("i,B,H,Nq,Nk,d,causal,dtype,scale", CASES,
+                         ids=[f"{c[0]}-B{c[1]}H{c[2]}q{c[3]}k{c[4]}d{c[5]}{'c' if c[6] else ''}" for c in CASES])
+def test_random_shape_matches_oracle(i, B, H, Nq, Nk, d, causal, dtype, scale):
+    say(f"random case {i}: B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal={causal} dtype={dtype} scale={scale}")
+    xq = W.custom(B, H, Nq, d, dtype=dtype, seed=1000 + i, tensors=("q",), scale=scale)
+    xkv = W.custom(B, H, Nk, d, dtype=dtype, seed=2000 + i, tensors=("k", "v"), scale=scale)
+    dq, dk, dv = to_device(xq["q"], dtype), to_device(xkv["k"], dtype), to_device(xkv["v"], dtype)
+    qm = mx.rotate_quantize(dq, mx.AXIS_HEAD_DIM, rotate=True)
+    km = mx.rotate_quantize(dk, mx.AXIS_HEAD_DIM, rotate=True)
+    vm = mx.rotate_quantize(dv, mx.AXIS_TOKEN, rotate=False)
+    stats = torch.empty((B, H, Nq, 2), dtype=torch.float32, device="cuda")
+    fstats = torch.empty_like(stats)
+    out = mx.forward(qm, km, vm, causal=causal, row_stats=stats)
+    fused = mx.forward_fused_q(dq, km, vm, causal=causal, row_stats=fstats)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), fused.view(torch.int32)), "two-call and fused-Q outputs differ"
+    assert torch.equal(stats.view(torch.int32), fstats.view(torch.int32))
+    ref = oracle.attention(xq["q"], xkv["k"], xkv["v"], dtype, B, H, Nq, d, causal=causal, kv_tile=KV_TILE,
+                           amb_delta=DELTA, Nk=Nk)
+    check_output(out.cpu().numpy(), ref, f"random case {i}", (Nk + KV_TILE - 1) // KV_TILE)
+    st = stats.cpu().numpy()
+    assert (st[..., 1] >= 1.0).all()
+    assert np.allclose(st[..., 0], ref["m"], rtol=1e-5, atol=1e-5)
