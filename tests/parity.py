@@ -41,7 +41,8 @@ DELTA = 2.0 ** -13
 U32 = 2.0 ** -24
 MAX_AMBIGUOUS_ROW_FRACTION = 0.005  # rows that may hold elements beyond ABS_TOL (within their allowance)
 MIN_AMBIGUOUS_ROW_CAP = 2           # ... a couple of rows on small cases
-MIN_ROWSUM_COVERAGE = 0.95     # row sums are compared on at least this share of rows
+MIN_ROWSUM_COVERAGE = 0.95     # row sums are compared on at least this share of rows ...
+MIN_UNCOMPARED_ROWS = 3        # ... or on all but this many (small cases)
 
 
 def say(*a):
@@ -129,10 +130,14 @@ def check_output(gpu, ref, label, n_tiles):
 def check_row_sums(gpu_rs, ref, label, rtol=2e-4, atol=2e-4):
     """Induced row sums of the reference modes against the oracle, on the rows
     where no close decision can move the row by more than ABS_TOL; those rows
-    must be at least MIN_ROWSUM_COVERAGE of all compared rows."""
+    must be at least MIN_ROWSUM_COVERAGE of all compared rows, or all but
+    MIN_UNCOMPARED_ROWS of them (a few rows of a small case: unrotated FP4
+    scores tie exactly or sit near a midpoint in a few percent of rows)."""
     unique = ref["amb"].max(axis=-1) <= ABS_TOL
     cov = float(unique.mean())
+    uncompared = int(unique.size - unique.sum())
     say(f"  [{label}] row sums compared on {int(unique.sum())}/{unique.size} rows ({100 * cov:.1f} %)")
-    assert cov >= MIN_ROWSUM_COVERAGE, f"{label}: row sums comparable on only {100 * cov:.1f} % of rows"
+    assert cov >= MIN_ROWSUM_COVERAGE or uncompared <= MIN_UNCOMPARED_ROWS, \
+        f"{label}: row sums comparable on only {100 * cov:.1f} % of rows"
     assert np.allclose(gpu_rs[unique], ref["rowsum"][unique], rtol=rtol, atol=atol), \
         f"{label}: max row-sum diff {float(np.abs(gpu_rs[unique] - ref['rowsum'][unique]).max()):.3e}"

@@ -9,7 +9,10 @@ compared with the oracle (MXAttention Alg. 2 in binary64) at the plain bar of
 tests/parity.py, and the two-call output (quantize, then forward) must equal
 the fused-Q forward's bit for bit: that one always runs the streaming kernel,
 so a case the resident-key kernel serves is checked against the streaming
-kernel too."""
+kernel too.  The self-attention cases also run the reference modes (the
+vanilla OCP baseline, post-normalization under OCP and UOS, PNQ's DIRECT
+counterpart; Sec. 4.2 Eq. 42, Sec. 5.5.2) with outputs and induced row sums
+against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -17,7 +20,7 @@ import torch
 import mxfp4_microscaled_bit_amd as mx
 import oracle
 import workloads as W
-from parity import DELTA, check_output, say, to_device
+from parity import DELTA, check_output, check_row_sums, say, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -65,3 +68,28 @@ def test_random_shape_matches_oracle(i, B, H, Nq, Nk, d, causal, dtype, scale):
     st = stats.cpu().numpy()
     assert (st[..., 1] >= 1.0).all()
     assert np.allclose(st[..., 0], ref["m"], rtol=1e-5, atol=1e-5)
+
+
+SELF_CASES = [c for c in CASES if c[3] == c[4]]
+REF_MODES = [(mx.P_DIRECT, mx.SCALE_OCP, False), (mx.P_POSTNORM, mx.SCALE_OCP, True),
+             (mx.P_POSTNORM, mx.SCALE_UOS, True), (mx.P_DIRECT, mx.SCALE_UOS, True)]
+
+
+@pytest.mark.parametrize("p_mode,rule,rotate", REF_MODES, ids=["direct-ocp-norot", "postnorm-ocp", "postnorm-uos",
+                                                                "direct-uos"])
+@pytest.mark.parametrize("i,B,H,Nq,Nk,d,causal,dtype,scale", SELF_CASES,
+                         ids=[f"{c[0]}-B{c[1]}H{c[2]}n{c[3]}d{c[5]}{'c' if c[6] else ''}" for c in SELF_CASES])
+def test_random_shape_reference_modes(i, B, H, Nq, Nk, d, causal, dtype, scale, p_mode, rule, rotate):
+    N = Nq
+    label = f"random case {i} mode {p_mode}/{rule}/{rotate}"
+    say(label)
+    x = W.custom(B, H, N, d, dtype=dtype, seed=3000 + i, scale=scale)
+    dq, dk, dv = (to_device(x[t], dtype) for t in "qkv")
+    sums = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    out = mx.quantize_reference_modes(dq, dk, dv, rule=rule, p_mode=p_mode, rotate=rotate, causal=causal,
+                                      row_sums=sums)
+    torch.cuda.synchronize()
+    ref = oracle.attention(x["q"], x["k"], x["v"], dtype, B, H, N, d, causal=causal, kv_tile=KV_TILE,
+                           rotate=rotate, rule=rule, p_mode=p_mode, amb_delta=DELTA)
+    check_output(out.cpu().numpy(), ref, label, (N + KV_TILE - 1) // KV_TILE)
+    check_row_sums(sums.cpu().numpy(), ref, label)
