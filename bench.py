@@ -28,10 +28,13 @@ With --separate-quantize the three tensors are quantized by three
 mxattn_rotate_quantize launches, and the JSON line adds per-launch rates for K
 and V.  With --fused-q the step quantizes K and V (two launches) and runs the
 forward entry point that rotates and quantizes Q in its own prologue (no Q^
-buffer).
+buffer).  With --part sweep or --part diagnostics the line times another part
+of the library on the same inputs instead: the Q_max sweep of Q, K and V over
+41 boundaries (priced against HBM), or the materialized-P diagnostics call
+(priced against the MXFP4 matrix peak).
 
     python bench.py [--steps K] [--warmup W] [--workload 2] [--separate-quantize] [--fused-q]
-                    [--no-cpu-baseline] [--no-probes]
+                    [--no-cpu-baseline] [--no-probes] [--part step|sweep|diagnostics]
 """
 from __future__ import annotations
 
@@ -176,6 +179,74 @@ def accuracy_vs_fp32(w, dev, out, n_rows: int = 256):
             "mean_rel": round(num / den, 6)}
 
 
+SWEEP_Q = [6.0 + 0.05 * i for i in range(41)]  # the Q_max grid 6.00, 6.05, ..., 8.00
+
+
+def measure_part(args, w, dev, stream):
+    """Time one of the other parts on the workload's inputs, resident in HBM:
+    `sweep` -- mxattn_scale_sweep of Q and K (head-dim blocks, rotated) and V
+    (token blocks) over SWEEP_Q, three launches per step, priced against HBM
+    (2 bytes read per element; the per-head sums are negligible);
+    `diagnostics` -- mxattn_p_diagnostics of (Q, K) with the UOS rule, the
+    statistics pass and the diagnostics pass (plus its own quantization of Q
+    and K), priced against the MXFP4 matrix peak with the score products of
+    both passes, 2 x 2d flops per visible pair (the forward's 4d)."""
+    import torch
+    import mxfp4_microscaled_bit_amd as mx
+
+    B, H, N, d = w.shape
+    Nk = w.kv_tokens
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    if args.part == "sweep":
+        outs = {t: torch.empty((B * H, len(SWEEP_Q)), dtype=torch.float64, device="cuda") for t in "qkv"}
+        ws = {t: torch.empty(max(1, mx.scale_sweep_workspace_bytes(B, H, dev[t].shape[2], d,
+                                                                   mx.AXIS_TOKEN if t == "v" else mx.AXIS_HEAD_DIM,
+                                                                   len(SWEEP_Q))), dtype=torch.uint8, device="cuda")
+              for t in "qkv"}
+
+        def run():
+            for t in "qkv":
+                axis = mx.AXIS_TOKEN if t == "v" else mx.AXIS_HEAD_DIM
+                mx.scale_sweep(dev[t], SWEEP_Q, axis=axis, rotate=(t != "v"), out=outs[t], workspace=ws[t])
+        elements = B * H * (N + 2 * Nk) * d
+        work, unit, peak, bound = elements * 2.0, "GB/s", HBM_PEAK_GBS, "hbm"
+        metric = "Q_max sweep of Q, K, V (per-head squared error, 41 boundaries; MXAttention Sec. 5.5.1)"
+    else:
+        out = torch.empty((B, H, N, 6), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, mx.p_diagnostics_workspace_bytes(B, H, N, d)), dtype=torch.uint8, device="cuda")
+        if Nk != N:
+            raise SystemExit("--part diagnostics needs self-attention (Nk = N)")
+
+        def run():
+            mx.p_diagnostics(dev["q"], dev["k"], rule=mx.SCALE_UOS, rotate=True, causal=w.causal, out=out,
+                             workspace=ws)
+        work, unit, peak, bound = w.flops(), "TFLOP/s", MFMA_FP4_PEAK_TFLOPS, "mfma"
+        metric = "materialized-P diagnostics (statistics + diagnostics passes; MXAttention Sec. 5.5.2)"
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = ev(), ev()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    rate = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+    return {
+        "metric": metric, "value": round(rate, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(wall * 1000.0 / args.steps, 4), "ms_per_call": round(ms, 4),
+        "higher_is_better": True, "dtype": "fp4", "data": "synthetic",
+        "config": {"workload": f"{w.name}: {w.describe()}", "part": args.part, "B": B, "H": H, "N": N, "d": d,
+                   "causal": w.causal, **({"Nk": Nk} if Nk != N else {})},
+        "roofline": {"bound": bound, "achieved": round(rate, 2), "peak": peak, "unit": unit,
+                     "frac": round(rate / peak, 4), "traffic": None,
+                     "work_per_call": work, "work_unit": "bytes" if unit == "GB/s" else "flops"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -189,6 +260,9 @@ def main():
                          "mxattn_rotate_quantize_qkv launch")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probes", action="store_true", help="skip the in-run throughput probes")
+    ap.add_argument("--part", choices=("step", "sweep", "diagnostics"), default="step",
+                    help="step: the benchmark (quantize + forward); sweep: the Q_max sweep of Q, K and V "
+                         "over 41 boundaries; diagnostics: the materialized-P diagnostics call")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="run three plain device-to-device copies of BYTES bytes and exit "
                          "(reference kernel for scaling the HBM byte counters)")
@@ -241,6 +315,9 @@ def main():
     log(f"inputs resident in HBM after {time.perf_counter() - t0:.1f}s")
 
     stream = torch.cuda.current_stream()
+    if args.part != "step":
+        print(json.dumps(measure_part(args, w, dev, stream)), flush=True)
+        return
     qm = mx.MXTensor.empty(B, H, N, d, mx.AXIS_HEAD_DIM)
     km = mx.MXTensor.empty(B, H, Nk, d, mx.AXIS_HEAD_DIM)
     vm = mx.MXTensor.empty(B, H, Nk, d, mx.AXIS_TOKEN)

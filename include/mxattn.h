@@ -233,7 +233,7 @@ mxattn_status mxattn_scale_sweep(const void* x, int32_t dtype, mxattn_shape shap
  * other errors are those of mxattn_scale_sweep; the result is bit-identical
  * to it.  MXATTN_ERR_SCRATCH if mxattn_scale_sweep_workspace_bytes(shape,
  * axis, n_q) exceeds MXATTN_SWEEP_SCRATCH_BYTES (e.g. B*H = 40, N = 32760,
- * d = 128 with 48 boundaries needs 1.97 MB; the limit admits about 8x that),
+ * d = 128 with 48 boundaries needs 0.49 MB; the limit admits about 34x that),
  * and nothing is enqueued.  Every call on one GPU shares that GPU's array:
  * calls that overlap on one GPU (other streams, other host threads) race and
  * give undefined sums; order them.  Nothing in the array needs clearing:

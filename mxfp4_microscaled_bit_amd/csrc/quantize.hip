@@ -240,7 +240,9 @@ __global__ __launch_bounds__(256, 7) void k_quantize_qkv(QTensor q, QTensor k, Q
 // most two candidate exponents, e(q_min) and one less, so each block is
 // quantized twice and every boundary only selects one of the two errors.
 
-constexpr int kSweepUnits = 4;  // work units per lane and workgroup pass
+// Work units (blocks, or channel pairs of a token block) per lane: enough
+// that the per-boundary workgroup reduction is a small share of the work.
+constexpr int kSweepUnits = 16;
 
 struct SweepQ {
   uint32_t qb[kSweepMax];  // binary32 bits of each boundary, rounded down
@@ -258,63 +260,105 @@ __device__ __forceinline__ void decode2(uint32_t w, float& lo, float& hi) {
 
 __device__ __forceinline__ double pow2d(int k) { return __longlong_as_double((long long)(1023 + k) << 52); }
 
-// 4^e * sum_i (v_i 2^-e - c_i)^2 in binary64, elements in order, where c_i
-// are the E2M1 values of the block's codes at exponent e.  Every step is exact
-// except the rounding of each square and each sum: the same per-block value
-// as the plain sum of (v_i - c_i 2^e)^2.
-__device__ __forceinline__ double block_sse(const float (&v)[32], int e) {
-  float y[32];
+// Eight E2M1 codes of v[8k .. 8k+7] at exponent e, exactly as block_codes
+// forms them (at the clamp e = -127 the values move up by 2^127 before a
+// unit-scale convert).
+__device__ __forceinline__ uint32_t codes8_at(const float (&v)[32], int k, int e) {
+  float y[8];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) y[i] = v[i];
-  const uint4 c = block_codes(y, e);
-  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
-  float g[32];  // E2M1 values of the codes (unit scale: exact)
+  for (int i = 0; i < 8; ++i) y[i] = e < -126 ? __builtin_amdgcn_ldexpf(v[8 * k + i], 127) : v[8 * k + i];
+  return cvt8(y, pow2f(e < -126 ? 0 : e));
+}
+
+// Squared quantization errors of one block at its two candidate exponents,
+// s = 4^e sum_i (v_i 2^-e - c_i)^2 in binary64, where c_i are the E2M1 values
+// of the block's codes at exponent e.  v_i 2^-e and its difference r_i to c_i
+// are exact, and r_i has at most 24 significant bits, so r_i^2 is exact too
+// and only the sums round (one fused multiply-add per element).  The elements go
+// eight at a time (one convert word each), and each sum is kept as four
+// interleaved partial sums, added pairwise at the end, so that its dependent
+// binary64 adds form four chains of eight instead of one of 32.
+__device__ __forceinline__ void block_sse_pair(const float (&v)[32], int e_hi, int e_lo, double& s_hi,
+                                               double& s_lo) {
+  double ph[4] = {0.0, 0.0, 0.0, 0.0}, pl[4] = {0.0, 0.0, 0.0, 0.0};
+  const double inv_hi = pow2d(-e_hi), inv_lo = pow2d(-e_lo);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    decode2<0>(w[k], g[8 * k + 0], g[8 * k + 1]);
-    decode2<1>(w[k], g[8 * k + 2], g[8 * k + 3]);
-    decode2<2>(w[k], g[8 * k + 4], g[8 * k + 5]);
-    decode2<3>(w[k], g[8 * k + 6], g[8 * k + 7]);
-  }
-  const double inv = pow2d(-e);
-  double s = 0.0;
+    const uint32_t wh = codes8_at(v, k, e_hi), wl = codes8_at(v, k, e_lo);
+    float gh[8], gl[8];  // E2M1 values of the codes (unit scale: exact)
+    decode2<0>(wh, gh[0], gh[1]);
+    decode2<1>(wh, gh[2], gh[3]);
+    decode2<2>(wh, gh[4], gh[5]);
+    decode2<3>(wh, gh[6], gh[7]);
+    decode2<0>(wl, gl[0], gl[1]);
+    decode2<1>(wl, gl[2], gl[3]);
+    decode2<2>(wl, gl[4], gl[5]);
+    decode2<3>(wl, gl[6], gl[7]);
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const double r = __dsub_rn(__dmul_rn((double)v[i], inv), (double)g[i]);
-    s = __dadd_rn(s, __dmul_rn(r, r));
+    for (int i = 0; i < 8; ++i) {
+      const double x = (double)v[8 * k + i];
+      const double rh = __dsub_rn(__dmul_rn(x, inv_hi), (double)gh[i]);
+      const double rl = __dsub_rn(__dmul_rn(x, inv_lo), (double)gl[i]);
+      ph[i & 3] = __fma_rn(rh, rh, ph[i & 3]);
+      pl[i & 3] = __fma_rn(rl, rl, pl[i & 3]);
+    }
   }
-  return __dmul_rn(s, pow2d(2 * e));
+  s_hi = __dmul_rn(__dadd_rn(__dadd_rn(ph[0], ph[1]), __dadd_rn(ph[2], ph[3])), pow2d(2 * e_hi));
+  s_lo = __dmul_rn(__dadd_rn(__dadd_rn(pl[0], pl[1]), __dadd_rn(pl[2], pl[3])), pow2d(2 * e_lo));
 }
 
 __device__ __forceinline__ void accumulate_block(const float (&v)[32], float M, const SweepQ& sq,
                                                  double (&acc)[kSweepMax]) {
   const int e_hi = scale_exponent<kRuleCeilQ>(M, sq.qmin);
   const int e_lo = e_hi > -127 ? e_hi - 1 : e_hi;
-  const double s_hi = block_sse(v, e_hi);
-  const double s_lo = block_sse(v, e_lo);
+  double s_hi, s_lo;
+  block_sse_pair(v, e_hi, e_lo, s_hi, s_lo);
+  // Boundary q_j takes e_hi unless ceil(log2(M / q_j)) <= e_hi - 1, i.e.
+  // unless M <= q_j 2^(e_hi - 1) (q_j <= 2 q_min leaves only those two).  With
+  // m = M 2^(1 - e_hi), exact in binary32 (m lies in (q_min, 2 q_min] when e_hi
+  // is not clamped; at the clamp e_lo = e_hi and a zero block has s_hi = s_lo
+  // = 0), that is m > q_j: the decision scale_exponent takes, with one
+  // compare.  Accumulators past nq collect unused sums and are never stored.
+  const float m = __builtin_amdgcn_ldexpf(M, 1 - e_hi);
 #pragma unroll
-  for (int j = 0; j < kSweepMax; ++j)
-    if (j < sq.nq) acc[j] = __dadd_rn(acc[j], scale_exponent<kRuleCeilQ>(M, sq.qb[j]) == e_hi ? s_hi : s_lo);
+  for (int j = 0; j < kSweepMax; ++j) acc[j] = __dadd_rn(acc[j], m > __uint_as_float(sq.qb[j]) ? s_hi : s_lo);
 }
 
-// Workgroup sums of acc[j] in a fixed order (xor butterfly in each wave, then
-// the four waves in order): bit-identical on every run.
+// Workgroup sums of acc[j] in a fixed order, through LDS in rounds of eight
+// boundaries: the 256 threads park acc[8r .. 8r+7]; thread t then adds the
+// eight values of boundary 8r + t/32 from threads 8(t%32) .. 8(t%32)+7 in
+// order, and 64 threads and then 8 add those partials in order (thread index
+// order throughout): bit-identical on every run.
 __device__ __forceinline__ void store_partial(double (&acc)[kSweepMax], int nq, double* __restrict__ out) {
-  __shared__ double red[4][kSweepMax];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ double park[256][9];  // [thread][boundary of the round], padded against bank conflicts
+  __shared__ double lvl1[8][32];
+  __shared__ double lvl2[8][4];
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < kSweepMax; ++j) {
-    if (j < nq) {
-      double s = acc[j];
+  for (int r = 0; r < kSweepMax / 8; ++r) {
+    if (8 * r < nq) {  // uniform
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) s = __dadd_rn(s, __shfl_xor(s, o));
-      if (lane == 0) red[wave][j] = s;
+      for (int k = 0; k < 8; ++k) park[t][k] = acc[8 * r + k];
+      __syncthreads();
+      {
+        const int jb = t >> 5, seg = t & 31;
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = __dadd_rn(s, park[8 * seg + i][jb]);
+        lvl1[jb][seg] = s;
+      }
+      __syncthreads();
+      if (t < 32) {
+        const int jb = t >> 2, q4 = t & 3;
+        double s = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s = __dadd_rn(s, lvl1[jb][8 * q4 + i]);
+        lvl2[jb][q4] = s;
+      }
+      __syncthreads();
+      if (t < 8 && 8 * r + t < nq)
+        out[8 * r + t] = __dadd_rn(__dadd_rn(lvl2[t][0], lvl2[t][1]), __dadd_rn(lvl2[t][2], lvl2[t][3]));
     }
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < nq) {
-    const int j = threadIdx.x;
-    out[j] = __dadd_rn(__dadd_rn(__dadd_rn(red[0][j], red[1][j]), red[2][j]), red[3][j]);
   }
 }
 

@@ -82,6 +82,17 @@ def test_bench_fused_q_step():
     assert d["forward"]["tflops"] > 0 and d["quantizer"]["quantize_v"]["us"] > 0
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("part,unit,bound", [("sweep", "GB/s", "hbm"), ("diagnostics", "TFLOP/s", "mfma")])
+def test_bench_other_parts(part, unit, bound):
+    """The Q_max sweep and the diagnostics call timed on their own, each with
+    a roofline against its own peak."""
+    d = _run("--workload", "1", "--steps", "2", "--warmup", "1", "--part", part)
+    assert d["config"]["part"] == part and d["unit"] == unit and d["value"] > 0
+    rf = d["roofline"]
+    assert rf["bound"] == bound and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3 and rf["work_per_call"] > 0
+
+
 def test_bench_refuses_more_than_one_gpu():
     """(CPU) the one-GPU scope is enforced before any GPU work."""
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
