@@ -451,7 +451,22 @@ __device__ __forceinline__ void decode_fp4x2(uint32_t w, float& lo, float& hi) {
 // saturation (y > 6), downward or upward rounding; the entropy term
 // P log2 P = y (a) in the same units.
 // dg: [row sum, zeroing, saturation, down, up, sum P log2 P].
-template <int D, int RULE>
+//
+// Per element only the sums that need a threshold are formed, without lane
+// masks (y >= 0, and g = 0 or g >= 1/2):
+//   up    max(g - y, 0);
+//   sat   min(6 - y, 0), which is g - y where y > 6 (the convert saturates
+//         to g = 6 there) and 0 elsewhere;
+//   zero  -y times z = max(1 - 4g, 0), which is 1 at g = 0 and 0 at any
+//         other grid value (a fused multiply-add, exact for z in {0, 1}).
+// The four classes of one element add up to g - y, so the block's down sum
+// is (sum g - sum y) - up - zero - sat, and its entropy term is
+// e sum y + sum y a' with a' = log2(P / 2^e) the convert's exponent argument.
+// Each product and difference is rounded on its own (no contraction), so the
+// errors are those of the convert's actual input y.  Invisible keys (masked
+// tiles only) have a' = -inf and y = 0; there a' is clamped to keep 0 a'
+// finite.
+template <int D, int RULE, bool MASKED>
 __device__ __forceinline__ void diag_block(const v16f& s0, const v16f& s1, float bmax, const RowState& rs,
                                            float gamma_f, float inv_gamma_f, float (&dg)[6]) {
   using F = FwdConsts<D, kModeDiag, RULE>;
@@ -461,8 +476,7 @@ __device__ __forceinline__ void diag_block(const v16f& s0, const v16f& s1, float
   if constexpr (RULE == kRuleOcp)
     if (bmax == rs.m) e = ocp_exponent_at_row_max(gamma_f, rs.rho);
   const float nb = -(rs.off + (float)e);
-  const float fe = (float)e;
-  float gsum = 0.0f, cz = 0.0f, cs = 0.0f, cd = 0.0f, cu = 0.0f, ent = 0.0f;
+  float gsum = 0.0f, ysum = 0.0f, cz = 0.0f, cs = 0.0f, cu = 0.0f, yarg = 0.0f;
   // eight elements at a time: exponentials, codes, their values, the sums
 #pragma unroll
   for (int c8 = 0; c8 < 4; ++c8) {
@@ -480,19 +494,19 @@ __device__ __forceinline__ void diag_block(const v16f& s0, const v16f& s1, float
     decode_fp4x2<3>(w, gq[6], gq[7]);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
+#pragma clang fp contract(off)
       const float g = gq[k], yy = y[k];
-      const float df = g - yy;
-      const bool zero = (g == 0.0f) & (yy > 0.0f);
-      const bool sat = yy > 6.0f;
       gsum += g;
-      cz += zero ? df : 0.0f;
-      cs += (!zero & sat) ? df : 0.0f;
-      cd += (!zero & !sat & (df < 0.0f)) ? df : 0.0f;
-      cu += (df > 0.0f) ? df : 0.0f;
-      ent += (yy > 0.0f) ? yy * (arg[k] + fe) : 0.0f;
+      ysum += yy;
+      cu += fmaxf(g - yy, 0.0f);
+      cz = fmaf(-yy, fmaxf(fmaf(-4.0f, g, 1.0f), 0.0f), cz);
+      cs += fminf(6.0f - yy, 0.0f);
+      yarg = fmaf(yy, MASKED ? fmaxf(arg[k], -0x1.fffffep+127f) : arg[k], yarg);
     }
     __builtin_amdgcn_sched_barrier(0);  // one group of eight live at a time
   }
+  const float cd = (((gsum - ysum) - cu) - cz) - cs;
+  const float ent = fmaf((float)e, ysum, yarg);
   // back from block units: P^ = g 2^e / gamma_f, P = y 2^e / gamma_f
   const float unit = __builtin_amdgcn_ldexpf(inv_gamma_f, e);
   dg[0] = fmaf(gsum, unit, dg[0]);
@@ -713,8 +727,8 @@ __device__ __forceinline__ void tile_step(const uint8_t* __restrict__ buf, int k
     }
   } else if constexpr (MODE == kModeDiag) {
     __builtin_amdgcn_sched_barrier(0);
-    diag_block<D, RULE>(s[0], s[1], bmax[0], rs, gamma_f, inv_gamma_f, dg);
-    diag_block<D, RULE>(s[2], s[3], bmax[1], rs, gamma_f, inv_gamma_f, dg);
+    diag_block<D, RULE, MASKED>(s[0], s[1], bmax[0], rs, gamma_f, inv_gamma_f, dg);
+    diag_block<D, RULE, MASKED>(s[2], s[3], bmax[1], rs, gamma_f, inv_gamma_f, dg);
   } else {
     const uint2 vsw = *reinterpret_cast<const uint2*>(buf + L::VS + 8 * lane);
     if constexpr (MODE != kModePostnorm) {
@@ -992,6 +1006,17 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
     tile_step<D, CAUSAL, MODE, RULE, true>(lds + (RESIDENT ? nfull : (nfull & 1)) * L::STAGE, nfull, nkeys, qop, qsc,
                                            qi, ones, one_sc, rs, acc, accl, held, lane, koff, dg, p.gamma_f,
                                            p.inv_gamma_f, pend);
+    // No later tile's maximum covers the scales of this tile's products: a
+    // read of every accumulator (which waits for all products so far) does,
+    // inside this block, before the register moves that lead into the
+    // deferred second half below can reuse them.
+    if constexpr (kDeferPV<D, CAUSAL> && MODE != kModeStats && MODE != kModeDiag) {
+      float all = accl[0];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) all += acc[ct][0];
+      keep_live(all, held[0], held[1], held[2], held[3]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if constexpr (kDeferPV<D, CAUSAL> && MODE != kModeStats && MODE != kModeDiag) {
     issue_pending<D>(pend, acc, accl, ones, one_sc);  // the last tile's second half
@@ -1056,11 +1081,9 @@ __device__ __forceinline__ void attention_qtile(const Params& p, uint8_t* lds, i
 // Under the causal mask query tile t visits t + 1 key tiles; a workgroup
 // takes the pair (nqt - 1 - i, i), nqt + 1 key tiles in all, so every
 // workgroup has the same work (the middle tile of an odd count runs alone).
-// Two workgroups (two waves per SIMD) per CU; the diagnostics pass keeps more
-// per-element state and runs with one, which gives it the accumulation
-// registers instead of scratch spills.
+// Two workgroups (two waves per SIMD) per CU.
 template <int D, bool CAUSAL, int MODE, int RULE, bool FUSEDQ>
-__global__ __launch_bounds__(256, MODE == kModeDiag ? 1 : 2) void k_attention(Params p) {
+__global__ __launch_bounds__(256, 2) void k_attention(Params p) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes<D>];
   const int tid = threadIdx.x;
   const int G = gridDim.x, bid = blockIdx.x;
