@@ -271,20 +271,28 @@ __device__ __forceinline__ uint32_t codes8_at(const float (&v)[32], int k, int e
 }
 
 // Squared quantization errors of one block at its two candidate exponents,
-// s = 4^e sum_i (v_i 2^-e - c_i)^2 in binary64, where c_i are the E2M1 values
-// of the block's codes at exponent e.  v_i 2^-e and its difference r_i to c_i
-// are exact, and r_i has at most 24 significant bits, so r_i^2 is exact too
-// and only the sums round (one fused multiply-add per element).  The elements go
+// s = 4^e sum_i (v_i 2^-e - c_i)^2, where c_i are the E2M1 values of the
+// block's codes at exponent e.  The residual r_i = v_i 2^-e - c_i is formed
+// by one binary32 fused multiply-add, exactly: v_i 2^-e is a power-of-two
+// scaling of v_i, and r_i has at most 24 significant bits (its lowest bit is
+// that of v_i 2^-e, its highest at most that of max(v_i 2^-e, 6)).  The one
+// exception is v_i 2^-e below 2^-126 (then c_i = 0), where the subnormal
+// result is off by at most 2^-150, 2^-250 of the block's own terms.  r_i^2
+// (at most 48 bits) is exact in binary64, so only the sums round: one
+// binary64 fused multiply-add per element and exponent.  The elements go
 // eight at a time (one convert word each), and each sum is kept as four
 // interleaved partial sums, added pairwise at the end, so that its dependent
-// binary64 adds form four chains of eight instead of one of 32.
+// binary64 adds form four chains of eight instead of one of 32.  CLAMP: some
+// block of the wave sits at e = -127, whose codes need the lifted convert.
+template <bool CLAMP>
 __device__ __forceinline__ void block_sse_pair(const float (&v)[32], int e_hi, int e_lo, double& s_hi,
                                                double& s_lo) {
   double ph[4] = {0.0, 0.0, 0.0, 0.0}, pl[4] = {0.0, 0.0, 0.0, 0.0};
-  const double inv_hi = pow2d(-e_hi), inv_lo = pow2d(-e_lo);
+  const float inv_hi = pow2f(-e_hi), inv_lo = pow2f(-e_lo);  // e in [-127, 126]: normal
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
-    const uint32_t wh = codes8_at(v, k, e_hi), wl = codes8_at(v, k, e_lo);
+    const uint32_t wh = CLAMP ? codes8_at(v, k, e_hi) : cvt8(&v[8 * k], pow2f(e_hi));
+    const uint32_t wl = CLAMP ? codes8_at(v, k, e_lo) : cvt8(&v[8 * k], pow2f(e_lo));
     float gh[8], gl[8];  // E2M1 values of the codes (unit scale: exact)
     decode2<0>(wh, gh[0], gh[1]);
     decode2<1>(wh, gh[2], gh[3]);
@@ -296,9 +304,8 @@ __device__ __forceinline__ void block_sse_pair(const float (&v)[32], int e_hi, i
     decode2<3>(wl, gl[6], gl[7]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const double x = (double)v[8 * k + i];
-      const double rh = __dsub_rn(__dmul_rn(x, inv_hi), (double)gh[i]);
-      const double rl = __dsub_rn(__dmul_rn(x, inv_lo), (double)gl[i]);
+      const double rh = (double)__fmaf_rn(v[8 * k + i], inv_hi, -gh[i]);
+      const double rl = (double)__fmaf_rn(v[8 * k + i], inv_lo, -gl[i]);
       ph[i & 3] = __fma_rn(rh, rh, ph[i & 3]);
       pl[i & 3] = __fma_rn(rl, rl, pl[i & 3]);
     }
@@ -312,7 +319,8 @@ __device__ __forceinline__ void accumulate_block(const float (&v)[32], float M, 
   const int e_hi = scale_exponent<kRuleCeilQ>(M, sq.qmin);
   const int e_lo = e_hi > -127 ? e_hi - 1 : e_hi;
   double s_hi, s_lo;
-  block_sse_pair(v, e_hi, e_lo, s_hi, s_lo);
+  if (__any(e_lo < -126)) block_sse_pair<true>(v, e_hi, e_lo, s_hi, s_lo);  // rare: tiny or zero blocks
+  else block_sse_pair<false>(v, e_hi, e_lo, s_hi, s_lo);
   // Boundary q_j takes e_hi unless ceil(log2(M / q_j)) <= e_hi - 1, i.e.
   // unless M <= q_j 2^(e_hi - 1) (q_j <= 2 q_min leaves only those two).  With
   // m = M 2^(1 - e_hi), exact in binary32 (m lies in (q_min, 2 q_min] when e_hi
