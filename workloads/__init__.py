@@ -221,3 +221,26 @@ def custom(B, H, N, d, dtype=BF16, seed=0, tensors=("q", "k", "v"), scale=1.0):
                 vals[b, h] = scale * _rng(seed, t, b, h).standard_normal((N, d))
         res[name] = to_bits(vals, dtype)
     return res
+
+
+def device_normal(B, H, N, d, dtype=BF16, seed=0, tensor="q", scale=1.0, device="cuda"):
+    """Standard-normal inputs drawn on the device, for shapes too large to draw
+    on the host (billions of elements): torch's seeded Philox generator on
+    `device`, keyed by (seed, tensor), rounded to the input dtype.  Returns a
+    torch tensor [B, H, N, d]; a test hands the oracle the 16-bit patterns of
+    the heads it checks, read back from this tensor."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(1_000_003 * int(seed) + 7919 * TENSOR_ID[tensor] + 17)
+    tdt = torch.bfloat16 if dtype == BF16 else torch.float16
+    out = torch.empty((B, H, N, d), dtype=tdt, device=device)
+    step = max(1, (1 << 28) // (N * d))  # heads per draw: at most 2^28 binary32 values at a time
+    flat = out.view(B * H, N, d)
+    for h0 in range(0, B * H, step):
+        h1 = min(B * H, h0 + step)
+        x = torch.randn((h1 - h0, N, d), generator=g, device=device, dtype=torch.float32)
+        if scale != 1.0:
+            x.mul_(scale)
+        flat[h0:h1].copy_(x)
+    return out
