@@ -13,7 +13,10 @@ forward kernels:
   * sampled output rows of the streaming forward (non-causal and causal) and
     of the resident-key forward (512 keys) against the oracle ([P1] Alg. 2)
     at the plain bar of tests/parity.py;
-  * the fused-Q forward equal to the two-call forward bit for bit."""
+  * the fused-Q forward equal to the two-call forward bit for bit;
+  * the other entry points at the same shape: the Q_max sweep along d and
+    along tokens, the materialized-P diagnostics and the POSTNORM reference
+    mode, each on the same heads against the oracle at its own test's bar."""
 import numpy as np
 import pytest
 import torch
@@ -21,8 +24,10 @@ import torch
 import mxfp4_microscaled_bit_amd as mx
 import oracle
 import workloads as W
-from parity import DELTA, check_output, say
+from parity import DELTA, check_output, check_row_sums, say
+from test_gpu_diagnostics import _check as check_diagnostics
 from test_gpu_quantize import _pack_rows, _pack_tokens
+from test_gpu_sweep import SWEEP, _check_sweep
 
 pytestmark = pytest.mark.gpu
 
@@ -109,4 +114,40 @@ def test_past_2_31_elements():
     say("  forward (resident keys, 512) done")
     _check_rows(out, xb, False, NK_CROSS, "large cross-attention")
     del out, qm, kxm, vxm, kx, vx, dev
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(600)
+def test_other_entry_points_past_2_31_elements():
+    say(f"large shape, other entry points: B={B} H={H} N={N} d={d}")
+    dev = {t: W.device_normal(B, H, N, d, seed=33, tensor=t) for t in "qkv"}
+    torch.cuda.synchronize()
+    bits = {t: _host_bits(dev[t], HEADS) for t in "qkv"}
+    idx = [b * H + h for b, h in HEADS]
+    for t, axis, rotate in (("q", mx.AXIS_HEAD_DIM, True), ("v", mx.AXIS_TOKEN, False)):
+        gpu = mx.scale_sweep(dev[t], SWEEP, axis=axis, rotate=rotate).cpu().numpy()
+        ref = oracle.scale_sweep(bits[t], W.BF16, 1, len(HEADS), N, d, SWEEP, axis=axis, rotate=rotate)
+        _check_sweep(gpu[idx], ref, f"large sweep {t}")
+
+    g = mx.p_diagnostics(dev["q"], dev["k"], rule=mx.SCALE_UOS, rotate=True, causal=False)
+    torch.cuda.synchronize()
+    ref, amb = oracle.p_diagnostics(bits["q"], bits["k"], W.BF16, 1, len(HEADS), N, d, causal=False, rows=ROWS,
+                                    amb_delta=DELTA)
+    gs = torch.stack([g[b, h][torch.from_numpy(ROWS).long().to(g.device)] for b, h in HEADS]).cpu().numpy()
+    check_diagnostics(gs[None], ref, amb, "large diagnostics")
+    del g
+
+    sums = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    out = mx.quantize_reference_modes(dev["q"], dev["k"], dev["v"], rule=mx.SCALE_UOS, p_mode=mx.P_POSTNORM,
+                                      rotate=True, causal=False, row_sums=sums)
+    torch.cuda.synchronize()
+    ref = oracle.attention(bits["q"], bits["k"], bits["v"], W.BF16, 1, len(HEADS), N, d, causal=False,
+                           rotate=True, rule=oracle.RULE_UOS, p_mode=oracle.P_POSTNORM, kv_tile=KV_TILE, rows=ROWS,
+                           amb_delta=DELTA)
+    sel = torch.from_numpy(ROWS).long().to(out.device)
+    o = torch.stack([out[b, h][sel] for b, h in HEADS]).cpu().numpy()
+    check_output(o[None], ref, "large POSTNORM/UOS", (N + KV_TILE - 1) // KV_TILE)
+    rs = torch.stack([sums[b, h][sel] for b, h in HEADS]).cpu().numpy()
+    check_row_sums(rs[None], ref, "large POSTNORM/UOS")
+    del out, sums, dev
     torch.cuda.empty_cache()
