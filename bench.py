@@ -182,6 +182,35 @@ def accuracy_vs_fp32(w, dev, out, n_rows: int = 256):
 SWEEP_Q = [6.0 + 0.05 * i for i in range(41)]  # the Q_max grid 6.00, 6.05, ..., 8.00
 
 
+ENTROPY_EDGES = (1.0, 2.0, 3.0, 4.0, 5.0)  # nats
+
+
+def diagnostics_report(diag) -> dict:
+    """The materialized-P row-sum statistics of MXAttention Sec. 5.5.2 (Fig. 7)
+    from per-row diagnostics [..., 6] (row sum, zeroing, saturation, down, up,
+    entropy in nats): the mean row sum (A), its mean decomposition by
+    outcome (B), and row sums binned by entropy (D), each bin with its share
+    of rows, mean row sum and share of over-normalized rows (sum > 1)."""
+    import numpy as np
+
+    d = np.asarray(diag, dtype=np.float64).reshape(-1, 6)
+    rs, ent = d[:, 0], d[:, 5]
+    rep = {"rows": int(d.shape[0]), "mean_row_sum": float(rs.mean()),
+           "mean_zeroing": float(d[:, 1].mean()), "mean_saturation": float(d[:, 2].mean()),
+           "mean_down": float(d[:, 3].mean()), "mean_up": float(d[:, 4].mean()),
+           "over_normalized_rows": float((rs > 1.0).mean()), "under_normalized_rows": float((rs < 1.0).mean())}
+    edges = (-np.inf,) + ENTROPY_EDGES + (np.inf,)
+    bins = []
+    for lo, hi in zip(edges[:-1], edges[1:]):
+        m = (ent >= lo) & (ent < hi)
+        label = f"<{hi:g}" if lo == -np.inf else (f">={lo:g}" if hi == np.inf else f"{lo:g}-{hi:g}")
+        bins.append({"entropy_nats": label, "share": float(m.mean()),
+                     "mean_row_sum": float(rs[m].mean()) if m.any() else None,
+                     "over_normalized": float((rs[m] > 1.0).mean()) if m.any() else None})
+    rep["entropy_bins"] = bins
+    return rep
+
+
 def measure_part(args, w, dev, stream):
     """Time one of the other parts on the workload's inputs, resident in HBM:
     `sweep` -- mxattn_scale_sweep of Q and K (head-dim blocks, rotated) and V
@@ -235,6 +264,43 @@ def measure_part(args, w, dev, stream):
     wall = time.perf_counter() - t0
     ms = e0.elapsed_time(e1) / args.steps
     rate = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
+    report = None
+    if args.part == "diagnostics":
+        # Fig. 7 of the pages, after the timed calls, under the path's UOS rule and the vanilla OCP rule (the
+        # pages do not say which rule their diagnostic uses): statistics at gamma = 1, then the
+        # pre-quantization global-scaling baseline (C).  A power of two in gamma cancels, so its fraction
+        # gamma_f in [1, 2) is scanned for the mean row sum closest to 1.
+        # Two readings of the baseline: the kernel returns Q(gamma P) / gamma (the factor taken out again,
+        # so it only moves rounding decisions); with the factor kept, Q(gamma P) = gamma (Q(gamma P) / gamma)
+        # and its row sums are gamma times the kernel's, so gamma near 1 / mean sets the mean to 1.
+        report = {}
+
+        def sums(rule, gamma):
+            mx.p_diagnostics(dev["q"], dev["k"], rule=rule, rotate=True, causal=w.causal, gamma=gamma, out=out,
+                             workspace=ws)
+            return out.cpu().numpy().reshape(-1, 6).astype("float64")
+
+        for name, rule in (("uos", mx.SCALE_UOS), ("ocp", mx.SCALE_OCP)):
+            scan, rep = [], None
+            for i in range(16):
+                gf = 1.0 + i / 16.0
+                g = sums(rule, gf)
+                if i == 0:
+                    rep = diagnostics_report(g)
+                scan.append({"gamma_f": gf, "mean_row_sum": float(g[:, 0].mean()),
+                             "over_normalized_rows": float((g[:, 0] > 1.0).mean())})
+            best = min(scan, key=lambda r: abs(r["mean_row_sum"] - 1.0))
+            kept = []
+            g0 = 1.0 / rep["mean_row_sum"]
+            for i in range(-8, 9):
+                gam = g0 * (1.0 + 0.005 * i)
+                rs = gam * sums(rule, gam)[:, 0]
+                kept.append({"gamma": gam, "mean_row_sum": float(rs.mean()), "over_normalized_rows": float((rs > 1.0).mean())})
+            rep["global_scaling"] = {
+                "factor_removed": {"scan": scan, "closest_to_unit_mean": best},
+                "factor_kept": {"scan": kept, "closest_to_unit_mean": min(kept, key=lambda r: abs(r["mean_row_sum"] - 1.0)),
+                                "over_normalized_rows_at_gamma_1": rep["over_normalized_rows"]}}
+            report[name] = rep
     return {
         "metric": metric, "value": round(rate, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(wall * 1000.0 / args.steps, 4), "ms_per_call": round(ms, 4),
@@ -244,6 +310,7 @@ def measure_part(args, w, dev, stream):
         "roofline": {"bound": bound, "achieved": round(rate, 2), "peak": peak, "unit": unit,
                      "frac": round(rate / peak, 4), "traffic": None,
                      "work_per_call": work, "work_unit": "bytes" if unit == "GB/s" else "flops"},
+        **({"report": report} if report is not None else {}),
     }
 
 

@@ -91,6 +91,44 @@ def test_bench_other_parts(part, unit, bound):
     assert d["config"]["part"] == part and d["unit"] == unit and d["value"] > 0
     rf = d["roofline"]
     assert rf["bound"] == bound and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3 and rf["work_per_call"] > 0
+    if part == "diagnostics":
+        for rule in ("uos", "ocp"):
+            rep = d["report"][rule]
+            assert rep["rows"] == 2 * 256 and 0.5 < rep["mean_row_sum"] < 1.5
+            assert abs(sum(b["share"] for b in rep["entropy_bins"]) - 1.0) < 1e-9
+            parts = rep["mean_zeroing"] + rep["mean_saturation"] + rep["mean_down"] + rep["mean_up"]
+            assert abs((rep["mean_row_sum"] - 1.0) - parts) < 1e-4
+            gs = rep["global_scaling"]["factor_removed"]
+            assert len(gs["scan"]) == 16 and gs["scan"][0]["gamma_f"] == 1.0
+            assert abs(gs["scan"][0]["mean_row_sum"] - rep["mean_row_sum"]) < 1e-12
+            assert gs["closest_to_unit_mean"] in gs["scan"]
+            gk = rep["global_scaling"]["factor_kept"]
+            assert len(gk["scan"]) == 17 and gk["closest_to_unit_mean"] in gk["scan"]
+            assert abs(gk["closest_to_unit_mean"]["mean_row_sum"] - 1.0) < 0.05  # small tensors: decisions jump with gamma
+
+
+def test_diagnostics_report_statistics():
+    """(CPU) the Fig. 7 statistics of the diagnostics line on a hand-made
+    array: means, over/under-normalized shares and the entropy bins."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    d = np.zeros((1, 2, 5, 6))
+    d[..., 0] = [[0.9, 1.1, 1.0, 0.8, 1.2], [0.9, 1.1, 1.0, 0.8, 1.2]]
+    d[..., 1] = -0.05
+    d[..., 4] = 0.02
+    d[..., 5] = [[0.5, 2.5, 6.0, 7.0, 1.0], [0.5, 2.5, 6.0, 7.0, 1.0]]
+    r = bench.diagnostics_report(d)
+    assert r["rows"] == 10 and abs(r["mean_row_sum"] - 1.0) < 1e-12
+    assert abs(r["mean_zeroing"] + 0.05) < 1e-12 and abs(r["mean_up"] - 0.02) < 1e-12
+    assert r["over_normalized_rows"] == 0.4 and r["under_normalized_rows"] == 0.4
+    bins = {b["entropy_nats"]: b for b in r["entropy_bins"]}
+    assert list(bins) == ["<1", "1-2", "2-3", "3-4", "4-5", ">=5"]
+    assert bins["<1"]["share"] == 0.2 and abs(bins["<1"]["mean_row_sum"] - 0.9) < 1e-12
+    assert bins["1-2"]["share"] == 0.2 and bins["1-2"]["over_normalized"] == 1.0  # entropy 1.0 opens its bin
+    assert bins[">=5"]["share"] == 0.4 and abs(bins[">=5"]["mean_row_sum"] - 0.9) < 1e-12
+    assert bins[">=5"]["over_normalized"] == 0.0
+    assert bins["3-4"]["share"] == 0.0 and bins["3-4"]["mean_row_sum"] is None
 
 
 def test_bench_refuses_more_than_one_gpu():
