@@ -211,6 +211,22 @@ def diagnostics_report(diag) -> dict:
     return rep
 
 
+def sweep_report(sse, qs) -> dict:
+    """Q_max optima of one tensor (MXAttention Sec. 5.5.1, Table 4) from its
+    per-head squared errors [heads, len(qs)]: the tensor's objective J(q)
+    (the sum over heads) with its argmin, and how often each q is a head's
+    argmin.  Ties go to the smallest q."""
+    import numpy as np
+
+    e = np.asarray(sse, dtype=np.float64)
+    J = e.sum(axis=0)
+    heads = np.argmin(e, axis=1)
+    counts = {f"{qs[j]:.2f}": int(c) for j, c in zip(*np.unique(heads, return_counts=True))}
+    j = int(np.argmin(J))
+    return {"tensor_optimum_q": round(float(qs[j]), 2), "J_at_optimum_over_J_at_7.25":
+            float(J[j] / J[int(np.argmin(np.abs(np.asarray(qs) - 7.25)))]), "head_optimum_counts": counts}
+
+
 def measure_part(args, w, dev, stream):
     """Time one of the other parts on the workload's inputs, resident in HBM:
     `sweep` -- mxattn_scale_sweep of Q and K (head-dim blocks, rotated) and V
@@ -265,6 +281,8 @@ def measure_part(args, w, dev, stream):
     ms = e0.elapsed_time(e1) / args.steps
     rate = work / (ms * 1e-3) / (1e9 if unit == "GB/s" else 1e12)
     report = None
+    if args.part == "sweep":
+        report = {t: sweep_report(outs[t].cpu().numpy(), SWEEP_Q) for t in "qkv"}
     if args.part == "diagnostics":
         # Fig. 7 of the pages, after the timed calls, under the path's UOS rule and the vanilla OCP rule (the
         # pages do not say which rule their diagnostic uses): statistics at gamma = 1, then the

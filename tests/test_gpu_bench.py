@@ -91,6 +91,11 @@ def test_bench_other_parts(part, unit, bound):
     assert d["config"]["part"] == part and d["unit"] == unit and d["value"] > 0
     rf = d["roofline"]
     assert rf["bound"] == bound and abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3 and rf["work_per_call"] > 0
+    if part == "sweep":
+        for t in "qkv":
+            rep = d["report"][t]
+            assert 6.0 <= rep["tensor_optimum_q"] <= 8.0 and 0 < rep["J_at_optimum_over_J_at_7.25"] <= 1.0
+            assert sum(rep["head_optimum_counts"].values()) == 2
     if part == "diagnostics":
         for rule in ("uos", "ocp"):
             rep = d["report"][rule]
@@ -129,6 +134,23 @@ def test_diagnostics_report_statistics():
     assert bins[">=5"]["share"] == 0.4 and abs(bins[">=5"]["mean_row_sum"] - 0.9) < 1e-12
     assert bins[">=5"]["over_normalized"] == 0.0
     assert bins["3-4"]["share"] == 0.0 and bins["3-4"]["mean_row_sum"] is None
+
+
+def test_sweep_report_optima():
+    """(CPU) Table 4's statistics of the sweep line on a hand-made array:
+    the tensor optimum minimizes the sum over heads, ties go to the smaller q."""
+    import numpy as np
+    sys.path.insert(0, ROOT)
+    import bench
+    qs = [6.0 + 0.05 * i for i in range(41)]
+    e = np.full((3, 41), 10.0)
+    e[0, 25] = 1.0   # head 0: 7.25
+    e[1, 24] = 2.0   # head 1: 7.20
+    e[2, 25] = 9.0   # head 2: 7.25 (J(7.25) = 20, J(7.20) = 22)
+    e[2, 30] = 9.0   # ... tied with 7.50: the smaller q wins
+    r = bench.sweep_report(e, qs)
+    assert r["tensor_optimum_q"] == 7.25 and r["J_at_optimum_over_J_at_7.25"] == 1.0
+    assert r["head_optimum_counts"] == {"7.20": 1, "7.25": 2}
 
 
 def test_bench_refuses_more_than_one_gpu():
