@@ -133,3 +133,22 @@ def test_diagnostics_reject_bad_arguments():
             mx.p_diagnostics(x, x, gamma=gamma)
     with pytest.raises(RuntimeError):
         mx.p_diagnostics(x, x, rule=mx.SCALE_CEIL_Q)
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
+def test_diagnostics_strided_layout_and_dtype(dtype):
+    """Q and K in [B, N, H, d] buffers viewed as [B, H, N, d] (no copy), bf16
+    and fp16, causal: every field equals the contiguous call's bit for bit and
+    the oracle's at the bar above."""
+    B, H, N, d = 2, 3, 200, 128
+    x = W.custom(B, N, H, d, dtype=dtype, seed=93, tensors=("q", "k"), scale=2.0)
+    dev = {t: to_device(x[t], dtype).permute(0, 2, 1, 3) for t in "qk"}
+    contig = {t: np.ascontiguousarray(x[t].transpose(0, 2, 1, 3)) for t in "qk"}
+    dc = {t: to_device(contig[t], dtype) for t in "qk"}
+    a = mx.p_diagnostics(dev["q"], dev["k"], causal=True)
+    b = mx.p_diagnostics(dc["q"], dc["k"], causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32)), "strided and contiguous diagnostics differ"
+    ref, amb = oracle.p_diagnostics(contig["q"], contig["k"], dtype, B, H, N, d, causal=True, rotate=True,
+                                    amb_delta=DELTA)
+    _check(a.cpu().numpy(), ref, amb, f"strided dtype={dtype}")

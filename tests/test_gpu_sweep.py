@@ -141,3 +141,22 @@ def test_sweep_wan_like_sampled_heads(t):
     _check_sweep(gpu[heads], ref, f"wan-like {t}")
     best = [SWEEP[int(np.argmin(r))] for r in gpu]
     say(f"  per-head argmin q: {dict(zip(*np.unique(best, return_counts=True)))}")
+
+
+@pytest.mark.parametrize("dtype", [W.BF16, W.FP16])
+def test_sweep_strided_layout_and_dtype(dtype):
+    """A [B, N, H, d] buffer viewed as [B, H, N, d] (no copy), bf16 and fp16:
+    the sweep equals the contiguous tensor's bit for bit, and the oracle's
+    sums on both axes."""
+    B, H, N, d = 2, 3, 150, 64
+    x = W.custom(B, N, H, d, dtype=dtype, seed=91, tensors=("k",), scale=3.0)["k"]  # physical [B, N, H, d]
+    dev = to_device(x, dtype).permute(0, 2, 1, 3)
+    contig = np.ascontiguousarray(x.transpose(0, 2, 1, 3))
+    dc = to_device(contig, dtype)
+    say(f"sweep strided dtype={dtype}")
+    for axis, rotate in ((mx.AXIS_HEAD_DIM, True), (mx.AXIS_TOKEN, False)):
+        a = mx.scale_sweep(dev, SWEEP, axis=axis, rotate=rotate).cpu().numpy()
+        b = mx.scale_sweep(dc, SWEEP, axis=axis, rotate=rotate).cpu().numpy()
+        assert np.array_equal(a, b), (axis, "strided and contiguous sums differ")
+        ref = oracle.scale_sweep(contig, dtype, B, H, N, d, SWEEP, axis=axis, rotate=rotate)
+        _check_sweep(a, ref, f"strided dtype={dtype} axis={axis}")
