@@ -201,8 +201,9 @@ size_t mxattn_scale_sweep_workspace_bytes(mxattn_shape shape, int32_t axis, int3
  * boundary q_j, the sum over the head's MXFP4 blocks of sum_i (x_i - x^_i)^2,
  * where x is exactly what mxattn_rotate_quantize sees (the decoded input,
  * Hadamard-rotated in binary32 if `rotate`) and x^ its MXFP4 reconstruction
- * under e = ceil(log2(M / q_j)).  Divided by the element count of a head it
- * is the tensor MSE the page's per-block optimum minimizes over q.
+ * under e = ceil(log2(M / q_j)).  Summed over the heads of a tensor and
+ * divided by its element count it is the tensor MSE whose argmin over q is
+ * the per-attention-block optimum of Table 4.
  *   x, dtype, shape, strides, axis, rotate   as in mxattn_rotate_quantize
  *   q_values  host array of n_q boundaries, 1 <= n_q <= MXATTN_SWEEP_MAX,
  *             each in [MXATTN_Q_MIN, MXATTN_Q_MAX], with max <= 2 min (so a
@@ -325,7 +326,8 @@ size_t mxattn_p_diagnostics_workspace_bytes(mxattn_shape shape);
  * every row (a first pass finds m and l), and quantize gamma P in aligned
  * 32-key blocks with `rule`: P^ = Q(gamma P) / gamma.  gamma is the
  * pre-quantization global scale of Fig. 7 (C); 1 gives the plain
- * diagnostic.  Writes, per query row, 6 floats:
+ * diagnostic.  (With the factor kept, Q(gamma P), a row sum is gamma times
+ * diag[.., 0].)  Writes, per query row, 6 floats:
  *   diag[.., 0]  sum_j P^_ij, the induced row sum (Fig. 7 (A));
  *   diag[.., 1..4]  the row-sum error sum_j (P^_ij - P_ij) split by the
  *                outcome of each element (Fig. 7 (B)): zeroing (P > 0 but
