@@ -75,7 +75,7 @@ def _load():
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int]
     lib.oracle_attention.restype = ctypes.c_int
     lib.oracle_attention.argtypes = [ctypes.c_void_p] + [ctypes.c_void_p] * 4 + [
-        ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 6
+        ctypes.c_void_p, ctypes.c_int32] + [ctypes.c_void_p] * 7
     _lib = lib
     return lib
 
@@ -265,7 +265,7 @@ def attention(q_bits, k_bits, v_bits, dtype, B, H, N, d, *, causal=False, rotate
     the number of key/value tokens (cross-attention; default N).
 
     Returns a dict with ``out`` [B,H,R,d], ``m``, ``l``, ``rowsum`` [B,H,R], ``amb``
-    and ``absmass`` [B,H,R,d] (all float64), R = len(rows) or N.
+    and ``absmass`` [B,H,R,d], ``amb_rowsum`` [B,H,R] (all float64), R = len(rows) or N.
     """
     for a in (q_bits, k_bits, v_bits):
         assert np.asarray(a).dtype == np.uint16
@@ -280,13 +280,14 @@ def attention(q_bits, k_bits, v_bits, dtype, B, H, N, d, *, causal=False, rotate
     rs = np.empty((B, H, R), np.float64)
     amb = np.empty((B, H, R, d), np.float64)
     absm = np.empty((B, H, R, d), np.float64)
+    ars = np.empty((B, H, R), np.float64)
     st = _strides(strides)
     qa, ka, va = (np.asarray(a) for a in (q_bits, k_bits, v_bits))
     if st is None:
         qa, ka, va = (np.ascontiguousarray(a) for a in (qa, ka, va))
     rc = _load().oracle_attention(ctypes.byref(cfg), _ptr(qa), _ptr(ka), _ptr(va), _ptr(st),
                                   _ptr(rows_a), R, _ptr(out), _ptr(m), _ptr(l), _ptr(rs), _ptr(amb),
-                                  _ptr(absm))
+                                  _ptr(absm), _ptr(ars))
     if rc != 0:
         raise ValueError("oracle_attention rejected its arguments")
-    return {"out": out, "m": m, "l": l, "rowsum": rs, "amb": amb, "absmass": absm}
+    return {"out": out, "m": m, "l": l, "rowsum": rs, "amb": amb, "absmass": absm, "amb_rowsum": ars}

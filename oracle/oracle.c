@@ -395,7 +395,7 @@ typedef struct {
   const int32_t* rows;
   int32_t n_rows;
   int32_t chunks_per_head, rows_per_chunk;
-  double *out, *m_out, *l_out, *rowsum, *amb, *absmass;
+  double *out, *m_out, *l_out, *rowsum, *amb, *absmass, *amb_rowsum;
 } attn_ctx;
 
 /* Dequantized (or plain) K and V of one head, and the query row, in binary64. */
@@ -565,6 +565,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
   double* tm = (double*)s; s += sizeof(double) * T;  /* m after tile t           */
   double* th = (double*)s; s += sizeof(double) * T;  /* sum of P^ over tile t    */
   double* tt = (double*)s; s += sizeof(double) * T;  /* sum of P~ over tile t    */
+  double* tdl = (double*)s; s += sizeof(double) * T; /* allowance of tile t's sum of P^ */
   double* blk = (double*)s; s += sizeof(double) * 32;
   float* buf = (float*)s;  s += sizeof(float) * d;
   uint8_t* codes = (uint8_t*)s;
@@ -614,7 +615,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
        * scale boundary.  The largest binary64 below 1 stands in for it: no
        * threshold of the block quantizer lies between the two. */
       const double pmax = (rho > 0.0 && 1.0 / ls == 1.0) ? nextafter(1.0, 0.0) : 1.0 / ls;
-      double sum_hat = 0.0;
+      double sum_hat = 0.0, sum_dp = 0.0;
       for (int j0 = 0; j0 < jvis; j0 += 32) {
         double pb[32], hb[32], db[32];
         for (int t = 0; t < 32; ++t)
@@ -624,8 +625,10 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
           sum_hat += hb[t];
           for (int ch = 0; ch < d; ++ch) o[ch] += hb[t] * V[(int64_t)(j0 + t) * d + ch];
           for (int ch = 0; ch < d; ++ch) am[ch] += hb[t] * fabs(V[(int64_t)(j0 + t) * d + ch]);
-          if (want_amb)
+          if (want_amb) {
+            sum_dp += db[t];
             for (int ch = 0; ch < d; ++ch) ao[ch] += db[t] * fabs(V[(int64_t)(j0 + t) * d + ch]);
+          }
         }
       }
       for (int ch = 0; ch < d; ++ch) orow[ch] = o[ch];
@@ -634,6 +637,8 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
       if (c->m_out) c->m_out[ridx] = ms;
       if (c->l_out) c->l_out[ridx] = ls;
       if (c->rowsum) c->rowsum[ridx] = sum_hat;
+      /* the induced row sum is sum_j P^_ij itself: a decision moves it by its own change */
+      if (c->amb_rowsum) c->amb_rowsum[ridx] = want_amb ? sum_dp : 0.0;
       continue;
     }
 
@@ -645,7 +650,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
     for (int tile = 0; tile < T; ++tile) {
       const int j0 = tile * Bc;
       int j1 = j0 + Bc < jvis ? j0 + Bc : jvis;
-      tm[tile] = -INFINITY; th[tile] = 0.0; tt[tile] = 0.0;
+      tm[tile] = -INFINITY; th[tile] = 0.0; tt[tile] = 0.0; tdl[tile] = 0.0;
       if (j1 <= j0) continue; /* no visible key for this row: a no-op */
       ++ntiles_seen;
       double smax = -INFINITY;
@@ -697,6 +702,7 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
           }
         }
         al = alpha * al + dl;
+        tdl[tile] = dl;
       }
       tm[tile] = m_new; th[tile] = sum_hat; tt[tile] = sum_til;
       m = m_new;                                     /* the running maximum moves on */
@@ -715,17 +721,21 @@ static void attn_item(void* vctx, int64_t item, void* scratch_raw) {
     }
     if (c->m_out) c->m_out[ridx] = m;
     if (c->l_out) c->l_out[ridx] = l;
-    if (c->rowsum) {
+    if (c->rowsum || c->amb_rowsum) {
       /* effective full-row form: beta_t = exp(m_t - m_final) [App. H Eq. 99] */
-      double num = 0.0, den = 0.0;
+      double num = 0.0, den = 0.0, anum = 0.0;
       for (int tile = 0; tile < T; ++tile) {
         if (tm[tile] == -INFINITY) continue;
         const double beta = exp(tm[tile] - m);
         num += beta * th[tile];
         den += beta * tt[tile];
+        anum += beta * tdl[tile];
       }
-      if (g->p_mode == ORACLE_P_DIRECT && quantize_p) c->rowsum[ridx] = num / den; /* Eq. 110 */
-      else c->rowsum[ridx] = num / l;                                              /* Eq. 51  */
+      const int direct_q = g->p_mode == ORACLE_P_DIRECT && quantize_p;
+      if (c->rowsum) c->rowsum[ridx] = direct_q ? num / den : num / l; /* Eq. 110 / Eq. 51 */
+      /* DIRECT: the decisions move only the numerator (by beta-weighted tile
+       * allowances); PNQ: the row sum is 1 whatever they decide */
+      if (c->amb_rowsum) c->amb_rowsum[ridx] = (want_amb && direct_q) ? anum / den : 0.0;
     }
   }
 }
@@ -734,7 +744,7 @@ int oracle_attention(const oracle_attn_cfg* cfg,
                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const int64_t* strides, const int32_t* rows, int32_t n_rows,
                      double* out, double* m_out, double* l_out, double* rowsum,
-                     double* amb, double* absmass) {
+                     double* amb, double* absmass, double* amb_rowsum) {
   if (!cfg || !q || !k || !v || !out) return -1;
   if (!shape_ok(cfg->B, cfg->H, cfg->N, cfg->d)) return -1;
   if (cfg->kv_tile < 32 || cfg->kv_tile % 32 != 0) return -1;
@@ -760,6 +770,7 @@ int oracle_attention(const oracle_attn_cfg* cfg,
   c.n_rows = n_rows;
   c.out = out; c.m_out = m_out; c.l_out = l_out; c.rowsum = rowsum; c.amb = amb;
   c.absmass = absmass;
+  c.amb_rowsum = amb_rowsum;
   const int64_t heads = (int64_t)cfg->B * cfg->H;
   int nth = cfg->nthreads > 0 ? cfg->nthreads : 1;
   int cph = (int)((2 * (int64_t)nth + heads - 1) / heads);
@@ -769,7 +780,7 @@ int oracle_attention(const oracle_attn_cfg* cfg,
   c.rows_per_chunk = (n_rows + cph - 1) / cph;
   const int N = Nk, d = cfg->d, T = (N + cfg->kv_tile - 1) / cfg->kv_tile;
   size_t scratch = sizeof(double) * ((size_t)2 * N * d + 4 * (size_t)d + N + 3 * (size_t)T * cfg->kv_tile +
-                                     3 * (size_t)T + 32) +
+                                     4 * (size_t)T + 32) +
                    sizeof(float) * d + 64;
   return run_pool(attn_item, &c, heads * cph, scratch, nth);
 }

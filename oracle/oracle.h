@@ -170,12 +170,18 @@ typedef struct {
  *                               (sum_j beta_j P^_j |v^_j| / l), the scale of
  *                               rounding errors of any accumulation order;
  *                               nullable
+ *   amb_rowsum [B][H][n_rows]   how far `rowsum` moves when those decisions
+ *                               go the other way (it is linear in P^: exact,
+ *                               not first-order): POSTNORM the sum of their
+ *                               changes, DIRECT the beta-weighted sum over
+ *                               (sum beta P~ 1), PNQ 0 (its row sum is 1
+ *                               whatever they decide); nullable
  * Returns 0, or -1 on a bad argument. */
 int oracle_attention(const oracle_attn_cfg* cfg,
                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
                      const int64_t* strides, const int32_t* rows, int32_t n_rows,
                      double* out, double* m_out, double* l_out, double* rowsum,
-                     double* amb, double* absmass);
+                     double* amb, double* absmass, double* amb_rowsum);
 
 /* Row-sum diagnostics of quantizing the materialized probabilities
  * [P1 Sec. 5.5.2, Fig. 7]: for each listed query row (rows / n_rows as in

@@ -127,12 +127,14 @@ static void run_attention(int N, int Nk, int d, int causal, int quant, int rule,
   cfg.q = 7.25;
   cfg.amb_delta = 0x1p-13;
   cfg.Nk = Nk == N ? 0 : Nk;
+  double* ars = (double*)malloc(no * sizeof(double));
   expect(oracle_attention(&cfg, q, k, v, NULL, n_rows > 0 ? rows : NULL, n_rows > 0 ? n_rows : N, out, m, l, rs, amb,
-                          am),
+                          am, ars),
          0, "attention");
+  free(ars);
   /* nullable outputs left out */
   expect(oracle_attention(&cfg, q, k, v, NULL, n_rows > 0 ? rows : NULL, n_rows > 0 ? n_rows : N, out, NULL, NULL,
-                          NULL, NULL, NULL),
+                          NULL, NULL, NULL, NULL),
          0, "attention, outputs only");
   if (Nk == N && quant && (rule == ORACLE_RULE_UOS || rule == ORACLE_RULE_OCP)) {
     double* diag = (double*)malloc(no * 6 * sizeof(double));
@@ -165,11 +167,11 @@ static void check_attention(void) {
   cfg.B = 1; cfg.H = 1; cfg.N = 8; cfg.d = 64; cfg.quant = 1; cfg.kv_tile = 40; cfg.nthreads = 1;
   uint16_t dummy[8 * 64] = {0};
   double out[8 * 64];
-  expect(oracle_attention(&cfg, dummy, dummy, dummy, NULL, NULL, 8, out, NULL, NULL, NULL, NULL, NULL), -1,
+  expect(oracle_attention(&cfg, dummy, dummy, dummy, NULL, NULL, 8, out, NULL, NULL, NULL, NULL, NULL, NULL), -1,
          "attention kv_tile=40");
   cfg.kv_tile = 32;
   cfg.d = 80;
-  expect(oracle_attention(&cfg, dummy, dummy, dummy, NULL, NULL, 8, out, NULL, NULL, NULL, NULL, NULL), -1,
+  expect(oracle_attention(&cfg, dummy, dummy, dummy, NULL, NULL, 8, out, NULL, NULL, NULL, NULL, NULL, NULL), -1,
          "attention d=80");
 }
 

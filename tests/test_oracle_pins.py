@@ -785,9 +785,12 @@ def test_postnorm_one_hot_row_allowance_follows_rho():
         assert (r["amb"].max() > 0) == open_
 
 
-def _forced_attention(qh, kh, vh, Bc, causal, rule, p_mode, delta, force, rows):
+def _forced_attention(qh, kh, vh, Bc, causal, rule, p_mode, delta, force, rows, rowsums=None):
     """Alg. 2 (PNQ / DIRECT) or the post-normalization mode re-stated over
-    dequantized q^, k^, v^ for the listed rows, with one hook:
+    dequantized q^, k^, v^ for the listed rows (and, into `rowsums` if given,
+    each row's induced row sum: sum Q(P) for post-normalization, Eq. 110's
+    (sum beta P^ 1) / (sum beta P~ 1) for DIRECT, (sum beta P^ 1) / l for
+    PNQ), with one hook:
     force(i, j0, p, ph, exact_ref) returns the quantized block used for row i,
     keys j0..j0+31 (ph is the plain block quantization of p).  exact_ref is 1
     for a block holding the row maximum's element when that maximum stands
@@ -808,16 +811,20 @@ def _forced_attention(qh, kh, vh, Bc, causal, rule, p_mode, delta, force, rows):
             alone = len(srt) < 2 or math.exp(srt[-2] - srt[-1]) < 1 - delta
             exact = alone and 2.0 ** -100 <= rho < 1
             P = e / e.sum()
-            o = np.zeros(d)
+            o, rs = np.zeros(d), 0.0
             for b0 in range(0, N, 32):
                 pb = np.zeros(32)
                 pb[:min(32, N - b0)] = P[b0:b0 + 32]
                 ref = 1.0 if exact and b0 <= jm < b0 + 32 else 0.0
                 ph = force(i, b0, pb, oracle.p_block_allowance(pb, rule)[0], ref)
                 o += ph[:min(32, N - b0)] @ vh[b0:b0 + 32]
+                rs += ph[:min(32, N - b0)].sum()
             out[i] = o
+            if rowsums is not None:
+                rowsums[i] = rs
             continue
         m, l, o = -np.inf, 0.0, np.zeros(d)
+        num = den = 0.0
         seen = []
         for j0 in range(0, N, Bc):
             idx = [j for j in range(j0, min(j0 + Bc, N)) if vis[j]]
@@ -836,9 +843,12 @@ def _forced_attention(qh, kh, vh, Bc, causal, rule, p_mode, delta, force, rows):
                 ref = 1.0 if alone and (pb == 1.0).any() else 0.0
                 ph[b0:b0 + 32] = force(i, j0 + b0, pb, oracle.p_block_allowance(pb, rule)[0], ref)
             l = a * l + (pt.sum() if p_mode == oracle.P_DIRECT else ph.sum())
+            num, den = a * num + ph.sum(), a * den + pt.sum()
             o = a * o + ph[np.array(idx) - j0] @ vh[idx]
             m = mn
         out[i] = o / l
+        if rowsums is not None:
+            rowsums[i] = num / den if p_mode == oracle.P_DIRECT else num / l
     return out
 
 
@@ -880,10 +890,16 @@ def test_allowance_bounds_every_flagged_decision_forced(p_mode, rule):
     r = oracle.attention(x["q"], x["k"], x["v"], W.BF16, 1, 1, N, d, causal=True, rotate=False, rule=rule,
                          p_mode=p_mode, kv_tile=Bc, amb_delta=delta)
     rows = list(range(N))
-    base = _forced_attention(qh, kh, vh, Bc, True, rule, p_mode, delta, lambda i, j0, p, ph, ref: ph, rows)
+    base_rs = {}
+    base = _forced_attention(qh, kh, vh, Bc, True, rule, p_mode, delta, lambda i, j0, p, ph, ref: ph, rows,
+                             rowsums=base_rs)
     for i in rows:
         assert np.allclose(base[i], r["out"][0, 0, i], rtol=1e-12, atol=1e-12)
+        assert abs(base_rs[i] - r["rowsum"][0, 0, i]) <= 1e-12
     amb = r["amb"][0, 0]
+    amb_rs = r["amb_rowsum"][0, 0]
+    if p_mode == oracle.P_PNQ:
+        assert (amb_rs == 0).all()  # PNQ's row sum is 1 whatever the decisions
     flips = 0
     for i in rows:
         blocks = []
@@ -898,9 +914,11 @@ def test_allowance_bounds_every_flagged_decision_forced(p_mode, rule):
             for alt in _alternatives(p, ph, dp, rule):
                 def swap(ii, jj, pp, hh, rr, alt=alt, j0=j0):
                     return alt if jj == j0 else hh
-                forced = _forced_attention(qh, kh, vh, Bc, True, rule, p_mode, delta, swap, [i])[i]
+                frs = {}
+                forced = _forced_attention(qh, kh, vh, Bc, True, rule, p_mode, delta, swap, [i], rowsums=frs)[i]
                 moved = np.abs(forced - base[i])
                 assert (moved <= amb[i] * (1 + 1e-9) + 1e-15).all(), (i, j0)
+                assert abs(frs[i] - base_rs[i]) <= amb_rs[i] * (1 + 1e-9) + 1e-15, (i, j0, "row sum")
                 flips += 1
     assert flips > 20
 
