@@ -224,6 +224,38 @@ def test_zero_queries_average_the_values():
     assert np.allclose(o, mean[:, :, None, :], rtol=1e-5, atol=1e-6)
 
 
+TIE_MODES = [(mx.P_PNQ, mx.SCALE_UOS, True), (mx.P_PNQ, mx.SCALE_OCP, True), (mx.P_DIRECT, mx.SCALE_OCP, False),
+             (mx.P_POSTNORM, mx.SCALE_OCP, True), (mx.P_POSTNORM, mx.SCALE_UOS, True)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("p_mode,rule,rotate", TIE_MODES, ids=["pnq-uos", "pnq-ocp", "direct-ocp", "postnorm-ocp",
+                                                               "postnorm-uos"])
+def test_tied_keys_match_oracle(p_mode, rule, rotate, causal):
+    """Keys built from five distinct rows, repeated: every score value recurs
+    about N/5 times, so many keys tie exactly at the running maximum (P~ = 1
+    on each, S26) and POSTNORM's l* counts them (S32).  Outputs and row
+    sums against the oracle on every row."""
+    B, H, N, d = 1, 2, 300, 128
+    x = W.custom(B, H, N, d, seed=13, scale=1.5)
+    k = x["k"].copy()
+    k[:, :, 5:] = np.concatenate([x["k"][:, :, :5]] * (N // 5 + 1), axis=2)[:, :, 5:N]
+    dev = {t: to_device(a, W.BF16) for t, a in (("q", x["q"]), ("k", k), ("v", x["v"]))}
+    label = f"tied keys mode {p_mode}/{rule}/{rotate} causal={causal}"
+    say(label)
+    sums = torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    ref_out = mx.quantize_reference_modes(dev["q"], dev["k"], dev["v"], rule=rule, p_mode=p_mode, rotate=rotate,
+                                          causal=causal, row_sums=sums)
+    torch.cuda.synchronize()
+    ref = oracle.attention(x["q"], k, x["v"], W.BF16, B, H, N, d, causal=causal, rotate=rotate, rule=rule,
+                           p_mode=p_mode, kv_tile=KV_TILE, amb_delta=DELTA)
+    check_output(ref_out.cpu().numpy(), ref, label, (N + KV_TILE - 1) // KV_TILE)
+    check_row_sums(sums.cpu().numpy(), ref, label)
+    if (p_mode, rule) == (mx.P_PNQ, mx.SCALE_UOS):  # the method itself: the same result through mxattn_forward
+        out, _ = run_forward(dev["q"], dev["k"], dev["v"], causal)
+        assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), "forward and PNQ reference mode differ"
+
+
 def test_single_key_and_first_causal_row_copy_v():
     B, H, d = 1, 2, 128
     for N, causal in ((1, False), (260, True)):
