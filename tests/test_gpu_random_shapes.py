@@ -1,6 +1,6 @@
 """Parity of the forward with the oracle on seeded random shapes.
 
-Twenty-four cases drawn once from a fixed seed: self-attention (causal or
+Seventy-two cases drawn once from a fixed seed: self-attention (causal or
 not) and cross-attention (Nq != Nk), d in {64, 128}, bf16 and fp16 inputs,
 standard normals scaled by 0.5 to 3 (from spread to peaked softmax rows), and
 token counts from 1 up to past the resident-key limit (Nk <= 512 at d = 128,
@@ -9,10 +9,10 @@ compared with the oracle (MXAttention Alg. 2 in binary64) at the plain bar of
 tests/parity.py, and the two-call output (quantize, then forward) must equal
 the fused-Q forward's bit for bit: that one always runs the streaming kernel,
 so a case the resident-key kernel serves is checked against the streaming
-kernel too.  The self-attention cases also run the reference modes (the
-vanilla OCP baseline, post-normalization under OCP and UOS, PNQ's DIRECT
-counterpart; Sec. 4.2 Eq. 42, Sec. 5.5.2) with outputs and induced row sums
-against the oracle."""
+kernel too.  The first sixteen self-attention cases also run the reference
+modes (the vanilla OCP baseline, post-normalization under OCP and UOS, PNQ's
+DIRECT counterpart; Sec. 4.2 Eq. 42, Sec. 5.5.2) with outputs and induced row
+sums against the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -27,7 +27,7 @@ pytestmark = pytest.mark.gpu
 KV_TILE = 128
 
 
-def _cases(n=24, seed=20261202):
+def _cases(n=72, seed=20261202):
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -70,7 +70,7 @@ def test_random_shape_matches_oracle(i, B, H, Nq, Nk, d, causal, dtype, scale):
     assert np.allclose(st[..., 0], ref["m"], rtol=1e-5, atol=1e-5)
 
 
-SELF_CASES = [c for c in CASES if c[3] == c[4]]
+SELF_CASES = [c for c in CASES if c[3] == c[4]][:16]
 REF_MODES = [(mx.P_DIRECT, mx.SCALE_OCP, False), (mx.P_POSTNORM, mx.SCALE_OCP, True),
              (mx.P_POSTNORM, mx.SCALE_UOS, True), (mx.P_DIRECT, mx.SCALE_UOS, True)]
 
