@@ -60,6 +60,14 @@ int main() {
     expect((int)mxattn_p_diagnostics_workspace_bytes(s), 0, "diagnostics workspace of an invalid shape");
   }
 
+  // the element limit: B H Np d = 2^36 is accepted, one more head is not
+  const mxattn_shape at_limit = {1, 8192, 65536, 128}, past_limit = {1, 8193, 65536, 128};
+  if (mxattn_mx_codes_bytes(at_limit, 0) != ((size_t)1 << 35)) {
+    fprintf(stderr, "codes_bytes at the 2^36-element limit: %zu\n", mxattn_mx_codes_bytes(at_limit, 0));
+    ++failures;
+  }
+  expect((int)mxattn_mx_codes_bytes(past_limit, 0), 0, "codes_bytes past the element limit");
+
   mxattn_mx_tensor out = {F, F + 4096, {0, 0, 0, 0}, 5, 5, 5};
   expect(mxattn_rotate_quantize(nullptr, 0, ok, nullptr, 0, 1, 0, &out, nullptr), MXATTN_ERR_NULL, "rq null x");
   expect(mxattn_rotate_quantize(F, 0, extremes[0], nullptr, 0, 1, 0, &out, nullptr), MXATTN_ERR_SHAPE, "rq shape");
